@@ -1,0 +1,205 @@
+"""Throughput of one POET-X layer training step (forward + backward) on one
+MI355X, through libpoetx.so.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config square]
+                    [--cpu-sample-tokens N | --no-cpu]
+
+A step is the whole hot path on one batch of synthetic tokens: Cayley-Neumann
+forward for both sides, the input-centric forward pass, the backward pass, and
+the Cayley-Neumann backward for both sides.  The permutation fold happens once
+before timing (once per inner loop).  Inputs are resident in HBM when timing
+starts.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "POET-X layer fwd+bwd tokens/s at 4096², b=256; % MFMA peak; CNP blocks/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def step_flops(cfg) -> float:
+    """Algorithmic flops of one step: 4mn + 6b(m+n) per token (Z and dV
+    products, the four per-token block products forward and backward, and the
+    two block reductions) plus 6 k b^2 (m+n) for the Cayley-Neumann passes."""
+    m, n, b, k, T = cfg.m, cfg.n, cfg.b, cfg.k, cfg.T
+    return T * (4.0 * m * n + 6.0 * b * (m + n)) + 6.0 * k * b * b * (m + n)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="square")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
+              "(the layer would shard over tokens with one all-reduce of the packed "
+              "gradients, which is not built here)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from orthogonal_reparameterized_02_amd import inputs as I
+    from orthogonal_reparameterized_02_amd import poetx as P
+    from orthogonal_reparameterized_02_amd._lib import lib
+    from orthogonal_reparameterized_02_amd.layer import POETXLayer
+
+    cfg = I.CONFIG_BY_NAME[args.config]
+    act = P.BF16 if cfg.dtype == "bf16" else P.F32
+    torch.cuda.set_device(0)
+    d = I.make_inputs(cfg, seed=args.seed, f64=False)
+
+    def dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act)
+    L.load(dev(d["W0"]), dev(d["theta_P"]), dev(d["theta_R"]), dev(d["perm_P"]), dev(d["perm_R"]))
+    x, dy = dev(d["x"]), dev(d["dy"])
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        L.step(x, dy)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps -----------------------------------
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        L.step(x, dy)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t0.elapsed_time(t1) / args.steps
+
+    # ---- per-stage times: the same K steps again with boundary events ----
+    # (events are recorded on the stream the kernels run on)
+    nev = 8
+    fwd_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    bwd_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    cnp_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for evs in fwd_ev + bwd_ev:      # torch creates the HIP events on first record
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+    import ctypes as C
+
+    def hook(evs):
+        arr = (C.c_void_p * nev)(*[e.cuda_event for e in evs])
+        rc = lib().poetx_set_stage_events(C.cast(arr, C.c_void_p), nev)
+        assert rc == 0, lib().poetx_last_error()
+
+    for s in range(args.steps):
+        cnp_ev[s][0].record(stream)
+        L.cnp()
+        cnp_ev[s][1].record(stream)
+        hook(fwd_ev[s])
+        P.poetx_layer_fwd(L.sh, x, L.G_P, L.G_R, L.W0f, L.perm_P, L.perm_R_inv, L.y, L.saved,
+                          L.ws_fwd)
+        hook(bwd_ev[s])
+        P.poetx_layer_bwd(L.sh, dy, L.GT_P, L.GT_R, L.W0fT, L.perm_P_inv, L.perm_R, L.saved,
+                          L.dx, L.dG_P, L.dG_R, L.ws_bwd)
+        lib().poetx_set_stage_events(None, 0)
+        cnp_ev[s][2].record(stream)
+        P.poetx_cnp_bwd(L.theta_R, L.dG_R, L.b, L.k, L.dtheta_R, L.act, ws=L.ws_cnp_bwd)
+        P.poetx_cnp_bwd(L.theta_P, L.dG_P, L.b, L.k, L.dtheta_P, L.act, ws=L.ws_cnp_bwd)
+        cnp_ev[s][3].record(stream)
+    torch.cuda.synchronize()
+
+    def mean_ms(evs, i, j):
+        return float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
+
+    fwd_names = ["gather_x", "blocks_P", "dense_Z", "blocks_R", "scatter_y"]
+    bwd_names = ["gather_dy", "blocks_R_bwd", "dG_R", "dense_dV", "blocks_P_bwd", "dG_P", "scatter_dx"]
+    stages = {nm: mean_ms(fwd_ev, i, i + 1) * 1e3 for i, nm in enumerate(fwd_names)}
+    stages.update({nm: mean_ms(bwd_ev, i, i + 1) * 1e3 for i, nm in enumerate(bwd_names)})
+    stages["cnp_fwd"] = mean_ms(cnp_ev, 0, 1) * 1e3
+    stages["cnp_bwd"] = mean_ms(cnp_ev, 2, 3) * 1e3
+
+    T, m, n, b = cfg.T, cfg.m, cfg.n, cfg.b
+    flops = step_flops(cfg)
+    peak = PEAK_BF16_TFLOPS if act == P.BF16 else PEAK_FP32_TFLOPS
+    tokens_per_s = T / (ms * 1e-3)
+    dense_us = stages["dense_Z"]
+    dense_tflops = 2.0 * T * m * n / (dense_us * 1e-6) / 1e12
+    nblocks = cfg.n_P + cfg.n_R
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if act == P.BF16 else "f32",
+        "data": "synthetic (seeded Gaussian activations and weights, random permutations)",
+        "config": {"workload": f"{cfg.name}: POET-X layer m={m} n={n} b={b} k={cfg.k} "
+                               f"T={T} tokens, {cfg.dtype} activations/W0, fp32 theta",
+                   "m": m, "n": n, "b": b, "k": cfg.k, "tokens": T, "seed": args.seed},
+        "mfma_peak_frac": flops / (ms * 1e-3) / (peak * 1e12),
+        "step_tflops": flops / (ms * 1e-3) / 1e12,
+        "cnp_blocks_per_s": {"fwd": nblocks / (stages["cnp_fwd"] * 1e-6),
+                             "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
+        "stages_us": {k: round(v, 2) for k, v in stages.items()},
+        "roofline": {"kernel": "dense_Z (Z = V W0f^T, bf16 MFMA GEMM)", "bound": "mfma",
+                     "achieved": dense_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": dense_tflops / peak, "traffic": None,
+                     "flops_per_launch": 2.0 * T * m * n, "avg_launch_us": dense_us},
+        "wall_s_timed": wall,
+    }
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, args.seed, min(args.cpu_sample_tokens, T))
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline(cfg, seed: int, ts: int) -> dict:
+    """The float64 oracle, as it stands, on the first `ts` tokens of the same
+    workload: forward and backward once (weights formed, CNP both sides)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    import oracle as O
+    from orthogonal_reparameterized_02_amd import inputs as I
+    d = I.make_inputs(cfg, seed=seed, T=ts)
+    t = time.perf_counter()
+    O.layer_fwd(d["x64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"], d["perm_R"],
+                cfg.b, cfg.k)
+    O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
+                d["perm_R"], cfg.b, cfg.k)
+    dt = time.perf_counter() - t
+    return {"value": ts / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {ts} of {cfg.T} tokens of the same layer, one forward+backward "
+                      f"in float64 NumPy ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,211 @@
+/*
+ * poetx.h -- C ABI of libpoetx.so: forward and backward pass of one POET-X
+ * reparameterized linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * The layer ("Reparameterized LLM Training via Orthogonal Equivalence
+ * Transformation", Abstract) computes y = x W^T with W = R W0 P, where W0 is
+ * a fixed random [m, n] weight and R, P are learnable orthogonal matrices.
+ * Following "POET-X: Memory-efficient LLM Training by Scaling Orthogonal
+ * Transformation" (technical summary, sections 2.1-2.4):
+ *   - R = Pi_R^T BD(G_R) Pi_R and P = Pi_P^T BD(G_P) Pi_P: block-diagonal
+ *     orthogonal matrices with b x b blocks, conjugated by random
+ *     permutations; permutation matrix of an index map: Pi[i, pi[i]] = 1;
+ *   - each block is G = (I+Q)(I + Q + ... + Q^k), the Cayley transform with
+ *     its inverse replaced by the Neumann series cut after Q^k, where Q is
+ *     skew-symmetric and only its strict upper triangle is stored (b(b-1)/2
+ *     parameters per block, row by row over i < j);
+ *   - the evaluation is input-centric: W is never formed; the input passes
+ *     through the P-side blocks, the fixed weight, then the R-side blocks;
+ *   - permutations are index maps; the two next to W0 are folded into it
+ *     once per inner loop: W0f[i, j] = W0[pi_R[i], pi_P[j]].
+ * With that fold the forward pass is
+ *   U = x[:, pi_P];  V_j = U_j G_Pj^T;  Z = V W0f^T;  S_i = Z_i G_Ri^T;
+ *   y[:, pi_R[c]] = S[:, c]
+ * (U_j: columns [j b, (j+1) b) of U), and the backward pass is
+ *   dS = dy[:, pi_R];  dZ_i = dS_i G_Ri;  dG_Ri = sum_t dS_i^T Z_i;
+ *   dV = dZ W0f;  dU_j = dV_j G_Pj;  dG_Pj = sum_t dV_j^T U_j;
+ *   dx[:, pi_P[c]] = dU[:, c];  dtheta = CNP^T(theta, dG).
+ * W0 is fixed and gets no gradient.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major and contiguous, base
+ *     aligned to 16 bytes.  The caller owns every buffer; the library never
+ *     allocates or frees device memory.
+ *   - Activation storage type `act` (POETX_F32 or POETX_BF16) applies to x,
+ *     y, dy, dx, W0, W0f, W0fT, G and GT.  theta, dtheta and dG are float32.
+ *     bf16 values are IEEE binary32 truncated to 16 bits; the library rounds
+ *     to nearest-even whenever it narrows.  Arithmetic accumulates in fp32.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream);
+ *     no call synchronizes the host.  Device faults surface at the caller's
+ *     next synchronization.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     any error nothing is written.  Permutations being valid is a
+ *     precondition that is not checked on the device.
+ *   - Entry points are thread-safe and keep no state between calls.
+ *   - poetx_last_error() returns a message for the calling thread's most
+ *     recent failure.
+ */
+#ifndef POETX_H
+#define POETX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define POETX_ABI_VERSION 1
+
+typedef enum {
+  POETX_OK = 0,
+  POETX_ERR_ARG = 1,          /* null pointer, bad size, misalignment      */
+  POETX_ERR_UNSUPPORTED = 2,  /* valid but not built (dtype / b pair)       */
+  POETX_ERR_WORKSPACE = 3,    /* workspace smaller than required            */
+  POETX_ERR_DEVICE = 4        /* HIP launch or device query failed          */
+} poetx_status;
+
+typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
+
+/* Shape of one layer.  m: outputs, n: inputs, b: block size (m % b == 0 and
+ * n % b == 0), k: Neumann order (>= 0), T: tokens (>= 1), act: poetx_dtype.
+ * Supported b: 8, 16, 32, 64, 128, 256, 512; float32 activations need
+ * b <= 64.  1 <= k <= 8 or k = 0. */
+typedef struct {
+  int32_t m, n, b, k, T;
+  int32_t act;
+} poetx_shape;
+
+typedef void* poetx_stream_t; /* a hipStream_t */
+
+/* ABI version of the loaded library (POETX_ABI_VERSION). */
+int32_t poetx_abi_version(void);
+
+/* Static string naming a status code. */
+const char* poetx_status_str(int32_t status);
+
+/* Message describing the calling thread's most recent error ("" if none). */
+const char* poetx_last_error(void);
+
+/*
+ * poetx_cnp_fwd -- Cayley-Neumann parameterization, forward
+ * ("POET-X ...", technical summary 2.4, "Efficient CNP"; the Italian page,
+ * "Sommario tecnico" 2, CNP bullet).
+ *   theta [nblk][b(b-1)/2] float32: packed strict upper triangle of each
+ *         skew-symmetric Q (Q[i][j] = theta[t], Q[j][i] = -theta[t],
+ *         t = i*b - i*(i+1)/2 + (j-i-1) for i < j).
+ *   G     [nblk][b][b] in g_dtype: G = (I+Q)(I + Q + ... + Q^k).
+ *   GT    [nblk][b][b] in g_dtype or NULL: G transposed (= CNP of -Q).
+ *   ws    workspace of poetx_cnp_workspace_bytes(nblk, b, k, 0, g_dtype) bytes
+ *         (may be NULL when that is 0).
+ * Errors: ERR_ARG (nblk < 1, k outside 0..8, b unsupported, null theta/G),
+ * ERR_UNSUPPORTED (float32 with b > 64), ERR_WORKSPACE, ERR_DEVICE.
+ */
+int32_t poetx_cnp_fwd(int32_t nblk, int32_t b, int32_t k, const float* theta,
+                      void* G, void* GT, int32_t g_dtype, void* ws,
+                      size_t ws_bytes, poetx_stream_t stream);
+
+/*
+ * poetx_cnp_bwd -- gradient of the packed parameters (technical summary 2.4:
+ * the backward pass reuses on-chip data and fuses, like the forward).
+ * Given dG = dL/dG [nblk][b][b] float32, writes
+ *   dtheta[t(i,j)] (=|+=) gQ[i][j] - gQ[j][i],  i < j,
+ * where gQ = dL/dQ for G(Q) above.  accumulate != 0 adds into dtheta.
+ *   prec: POETX_F32 (fp32 arithmetic, b <= 64) or POETX_BF16 (bf16 MFMA
+ *         operands with fp32 accumulation), the class of the layer's G.
+ *   ws: poetx_cnp_workspace_bytes(nblk, b, k, 1, prec) bytes.
+ * Errors as poetx_cnp_fwd (null dG/dtheta -> ERR_ARG).
+ */
+int32_t poetx_cnp_bwd(int32_t nblk, int32_t b, int32_t k, const float* theta,
+                      const float* dG, float* dtheta, int32_t accumulate,
+                      int32_t prec, void* ws, size_t ws_bytes,
+                      poetx_stream_t stream);
+
+/* Workspace bytes for poetx_cnp_fwd (which = 0) or poetx_cnp_bwd (1) with
+ * float32 (act = POETX_F32) or bf16 (POETX_BF16) activations;
+ * 0 on bad arguments. */
+size_t poetx_cnp_workspace_bytes(int32_t nblk, int32_t b, int32_t k,
+                                 int32_t which, int32_t act);
+
+/*
+ * poetx_fold_perm -- permutation reduction (technical summary 2.2: two of
+ * the four forward permutations are merged into the weight before the inner
+ * loop).  Pure data movement, bit-exact:
+ *   W0f[i][j]  = W0[perm_R[i]][perm_P[j]]        [m][n]
+ *   W0fT[j][i] = W0f[i][j]                       [n][m], or NULL
+ *   perm_R_inv[perm_R[i]] = i  (m entries), perm_P_inv likewise (n), or NULL.
+ * W0fT is the layout the backward dV = dZ W0f product reads.
+ * Errors: ERR_ARG (m, n < 1, null W0/perm/W0f, dt not F32/BF16).
+ */
+int32_t poetx_fold_perm(int32_t m, int32_t n, int32_t dt, const void* W0,
+                        const int32_t* perm_R, const int32_t* perm_P, void* W0f,
+                        void* W0fT, int32_t* perm_R_inv, int32_t* perm_P_inv,
+                        poetx_stream_t stream);
+
+/*
+ * poetx_layer_fwd -- input-centric forward pass (technical summary 2.1-2.3).
+ *   x     [T][n]        input (act)
+ *   G_P   [n/b][b][b]   P-side blocks (act), from poetx_cnp_fwd
+ *   G_R   [m/b][b][b]   R-side blocks (act)
+ *   W0f   [m][n]        folded weight (act), from poetx_fold_perm
+ *   perm_P [n], perm_R_inv [m]  int32 index maps
+ *   y     [T][m]        output (act)
+ *   saved poetx_saved_bytes(sh) bytes: activations kept for the backward
+ *         pass (U = x[:, pi_P] then Z, both [T][*] act); the caller keeps it
+ *         alive and unmodified until poetx_layer_bwd.
+ *   ws    poetx_workspace_bytes(sh, 0) bytes of scratch.
+ * Errors: ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE.
+ */
+int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P,
+                        const void* G_R, const void* W0f, const int32_t* perm_P,
+                        const int32_t* perm_R_inv, void* y, void* saved,
+                        void* ws, size_t ws_bytes, poetx_stream_t stream);
+
+/*
+ * poetx_layer_bwd -- backward pass.
+ *   dy    [T][m]        dL/dy (act)
+ *   GT_P  [n/b][b][b]   P-side blocks transposed (act), from poetx_cnp_fwd
+ *   GT_R  [m/b][b][b]   R-side blocks transposed (act)
+ *   W0fT  [n][m]        folded weight transposed (act)
+ *   perm_P_inv [n], perm_R [m]  int32 index maps
+ *   saved as written by poetx_layer_fwd for the same shape and inputs
+ *   dx    [T][n]        dL/dx (act)
+ *   dG_P  [n/b][b][b], dG_R [m/b][b][b]  float32 dL/dG (overwritten)
+ *   ws    poetx_workspace_bytes(sh, 1) bytes of scratch.
+ * The token reduction of dG is deterministic (no atomics): repeated calls
+ * give bitwise-equal results.
+ * Errors: ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE.
+ */
+int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P,
+                        const void* GT_R, const void* W0fT,
+                        const int32_t* perm_P_inv, const int32_t* perm_R,
+                        const void* saved, void* dx, float* dG_P, float* dG_R,
+                        void* ws, size_t ws_bytes, poetx_stream_t stream);
+
+/*
+ * poetx_set_stage_events -- timing hook for profilers and benchmarks.
+ * While set, each poetx_layer_fwd / poetx_layer_bwd call on the calling
+ * thread records events[i] (hipEvent_t handles owned by the caller) on its
+ * stream at stage boundary i:
+ *   forward  (count >= 6): 0 | gather x | 1 | P-side blocks | 2 | W0 product
+ *            | 3 | R-side blocks | 4 | scatter y | 5
+ *   backward (count >= 8): 0 | gather dy | 1 | R-side blocks | 2 | dG_R |
+ *            3 | W0 product | 4 | P-side blocks | 5 | dG_P | 6 | scatter dx | 7
+ * When two stages run in one kernel their shared boundary is recorded
+ * twice, back to back.  events = NULL clears the hook.
+ * Errors: ERR_ARG (events non-NULL and count < 8).
+ */
+int32_t poetx_set_stage_events(void* const* events, int32_t count);
+
+/* Scratch bytes for poetx_layer_fwd (which = 0) or poetx_layer_bwd (1);
+ * 0 on bad arguments. */
+size_t poetx_workspace_bytes(const poetx_shape* sh, int32_t which);
+
+/* Bytes of the saved-activation buffer; 0 on bad arguments. */
+size_t poetx_saved_bytes(const poetx_shape* sh);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POETX_H */

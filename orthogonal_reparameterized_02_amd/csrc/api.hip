@@ -1,0 +1,439 @@
+// C ABI of libpoetx.so: host-side validation, workspace layout and dispatch.
+// Declarations and argument documentation: include/poetx.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/poetx.h"
+#include "kernels.h"
+
+using namespace poetx;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int32_t fail(int32_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+int32_t ok() {
+  g_err[0] = '\0';
+  return POETX_OK;
+}
+
+int32_t dev_fail(hipError_t e, const char* where) {
+  return fail(POETX_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define NEED_PTR(p)                                                                  \
+  do {                                                                               \
+    if (!(p)) return fail(POETX_ERR_ARG, "%s: null pointer '%s'", fn, #p);           \
+    if (!aligned16(p)) return fail(POETX_ERR_ARG, "%s: '%s' not 16-byte aligned", fn, #p); \
+  } while (0)
+#define OPT_PTR(p)                                                                   \
+  do {                                                                               \
+    if ((p) && !aligned16(p))                                                        \
+      return fail(POETX_ERR_ARG, "%s: '%s' not 16-byte aligned", fn, #p);            \
+  } while (0)
+
+bool b_supported(int b) {
+  return b == 8 || b == 16 || b == 32 || b == 64 || b == 128 || b == 256 || b == 512;
+}
+
+constexpr int K_MAX = 8;
+constexpr int SMALL_B_MAX = 64;  // LDS-resident fp32 Cayley-Neumann kernels
+
+size_t es_of(int act) { return act == POETX_BF16 ? 2 : 4; }
+
+size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
+
+// the MFMA Cayley-Neumann panels run for bf16 blocks of 64..512
+bool cnp_uses_panel(int b, int act) { return act == POETX_BF16 && b >= 64; }
+
+int32_t check_cnp_args(const char* fn, int32_t nblk, int32_t b, int32_t k, int32_t act) {
+  if (nblk < 1) return fail(POETX_ERR_ARG, "%s: nblk=%d < 1", fn, nblk);
+  if (!b_supported(b)) return fail(POETX_ERR_ARG, "%s: b=%d not in {8,16,32,64,128,256,512}", fn, b);
+  if (k < 0 || k > K_MAX) return fail(POETX_ERR_ARG, "%s: k=%d outside 0..%d", fn, k, K_MAX);
+  if (act != POETX_F32 && act != POETX_BF16) return fail(POETX_ERR_ARG, "%s: dtype %d", fn, act);
+  if (act == POETX_F32 && b > SMALL_B_MAX)
+    return fail(POETX_ERR_UNSUPPORTED, "%s: float32 blocks need b <= %d (b=%d)", fn, SMALL_B_MAX, b);
+  return POETX_OK;
+}
+
+int32_t check_shape(const char* fn, const poetx_shape* sh) {
+  if (!sh) return fail(POETX_ERR_ARG, "%s: null shape", fn);
+  if (sh->m < 1 || sh->n < 1 || sh->T < 1)
+    return fail(POETX_ERR_ARG, "%s: m=%d n=%d T=%d must be >= 1", fn, sh->m, sh->n, sh->T);
+  if (!b_supported(sh->b))
+    return fail(POETX_ERR_ARG, "%s: b=%d not in {8,16,32,64,128,256,512}", fn, sh->b);
+  if (sh->m % sh->b || sh->n % sh->b)
+    return fail(POETX_ERR_ARG, "%s: m=%d and n=%d must be multiples of b=%d", fn, sh->m, sh->n, sh->b);
+  if (sh->k < 0 || sh->k > K_MAX) return fail(POETX_ERR_ARG, "%s: k=%d outside 0..%d", fn, sh->k, K_MAX);
+  if (sh->act != POETX_F32 && sh->act != POETX_BF16)
+    return fail(POETX_ERR_ARG, "%s: act dtype %d", fn, sh->act);
+  if (sh->act == POETX_F32 && sh->b > SMALL_B_MAX)
+    return fail(POETX_ERR_UNSUPPORTED, "%s: float32 layers need b <= %d (b=%d)", fn, SMALL_B_MAX, sh->b);
+  return POETX_OK;
+}
+
+size_t cnp_ws(int nblk, int b, int k, int which, int act) {
+  const size_t bb = (size_t)b * b;
+  if (!cnp_uses_panel(b, act)) return which == 0 ? 0 : align_up((size_t)nblk * k * bb * 4);
+  if (which == 0) return align_up(nblk * bb * 2);
+  return align_up(nblk * bb * 2) + align_up((size_t)k * nblk * bb * 2) + align_up(nblk * bb * 4);
+}
+
+
+// ---- timing hook: stage-boundary events, per calling thread ---------------
+thread_local hipEvent_t g_stage_ev[8];
+thread_local int g_stage_on = 0;
+
+inline void mark(int i, hipStream_t s) {
+  if (g_stage_on) (void)hipEventRecord(g_stage_ev[i], s);
+}
+
+// MFMA kernels carry bf16 layers with b >= 64; everything else takes the
+// portable tiled kernels
+inline bool use_mfma(const poetx_shape* sh) { return sh->act == POETX_BF16 && sh->b >= 64; }
+
+// workspace layout of the layer calls
+struct FwdWs { size_t V, S, total; };
+struct BwdWs { size_t dS, dZ, dV, dU, part, total; };
+
+FwdWs fwd_ws(const poetx_shape* sh) {
+  const size_t es = es_of(sh->act), T = sh->T;
+  FwdWs w;
+  w.V = 0;
+  w.S = w.V + align_up(T * sh->n * es);
+  w.total = w.S + align_up(T * sh->m * es);
+  return w;
+}
+
+BwdWs bwd_ws(const poetx_shape* sh) {
+  const size_t es = es_of(sh->act), T = sh->T;
+  BwdWs w;
+  w.dS = 0;
+  w.dZ = w.dS + align_up(T * sh->m * es);
+  w.dV = w.dZ + align_up(T * sh->m * es);
+  w.dU = w.dV + align_up(T * sh->n * es);
+  w.part = w.dU + align_up(T * sh->n * es);
+  size_t part = 0;
+  if (use_mfma(sh)) {
+    const size_t pr = tn_partial_bytes(sh->m / sh->b, sh->b, sh->T);
+    const size_t pp = tn_partial_bytes(sh->n / sh->b, sh->b, sh->T);
+    part = align_up(pr > pp ? pr : pp);
+  }
+  w.total = w.part + part;
+  return w;
+}
+
+// saved activations: U = x[:, pi_P] then Z
+size_t saved_U(const poetx_shape*) { return 0; }
+size_t saved_Z(const poetx_shape* sh) { return align_up((size_t)sh->T * sh->n * es_of(sh->act)); }
+size_t saved_total(const poetx_shape* sh) {
+  return saved_Z(sh) + align_up((size_t)sh->T * sh->m * es_of(sh->act));
+}
+
+template <typename TS> TS* at(void* base, size_t off) {
+  return reinterpret_cast<TS*>(reinterpret_cast<char*>(base) + off);
+}
+template <typename TS> const TS* at(const void* base, size_t off) {
+  return reinterpret_cast<const TS*>(reinterpret_cast<const char*>(base) + off);
+}
+
+// ---- the layer passes, per storage type ---------------------------------
+// C[bt] = A[bt] B[bt]^T
+template <typename TS>
+hipError_t nt(bool mfma, int batch, int M, int N, int K, const TS* A, long lda, long sA,
+              const TS* B, long ldb, long sB, TS* C, long ldc, long sC, hipStream_t s) {
+  if constexpr (sizeof(TS) == 2) {
+    if (mfma && mfma_nt_ok(M, N, K))
+      return launch_mfma_nt(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+  }
+  return launch_simple_nt<TS>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+}
+
+// out[bt] = A_bt^T B_bt over T tokens, D x D blocks at column offsets bt*D
+template <typename TS>
+hipError_t tn(bool mfma, int batch, int D, int T, const TS* A, long lda, const TS* B, long ldb,
+              float* out, float* partials, hipStream_t s) {
+  if constexpr (sizeof(TS) == 2) {
+    if (mfma) return launch_mfma_tn(batch, D, T, A, lda, D, B, ldb, D, out, partials, s);
+  }
+  return launch_simple_tn<TS>(batch, D, D, T, A, lda, D, B, ldb, D, out, D, (long)D * D, s);
+}
+
+template <typename TS>
+int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const TS* G_R,
+                       const TS* W0f, const int32_t* perm_P, const int32_t* perm_R_inv, TS* y,
+                       void* saved, void* ws, hipStream_t s) {
+  const int m = sh->m, n = sh->n, b = sh->b, T = sh->T;
+  const int es = (int)sizeof(TS);
+  const bool mf = use_mfma(sh);
+  const FwdWs w = fwd_ws(sh);
+  TS* U = at<TS>(saved, saved_U(sh));
+  TS* Z = at<TS>(saved, saved_Z(sh));
+  TS* V = at<TS>(ws, w.V);
+  TS* S = at<TS>(ws, w.S);
+  const long bb = (long)b * b;
+  hipError_t e;
+  mark(0, s);
+  // U = x[:, pi_P]
+  if ((e = launch_permute_cols(T, n, es, x, perm_P, U, s)) != hipSuccess) return dev_fail(e, "gather x");
+  mark(1, s);
+  // V_j = U_j G_Pj^T
+  if ((e = nt<TS>(mf, n / b, T, b, b, U, n, b, G_P, b, bb, V, n, b, s)) != hipSuccess)
+    return dev_fail(e, "P-side blocks");
+  mark(2, s);
+  // Z = V W0f^T
+  if ((e = nt<TS>(mf, 1, T, m, n, V, n, 0, W0f, n, 0, Z, m, 0, s)) != hipSuccess)
+    return dev_fail(e, "W0 product");
+  mark(3, s);
+  // S_i = Z_i G_Ri^T
+  if ((e = nt<TS>(mf, m / b, T, b, b, Z, m, b, G_R, b, bb, S, m, b, s)) != hipSuccess)
+    return dev_fail(e, "R-side blocks");
+  mark(4, s);
+  // y[:, pi_R[c]] = S[:, c]  <=>  y = S[:, pi_R^{-1}]
+  if ((e = launch_permute_cols(T, m, es, S, perm_R_inv, y, s)) != hipSuccess)
+    return dev_fail(e, "scatter y");
+  mark(5, s);
+  return ok();
+}
+
+template <typename TS>
+int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, const TS* GT_R,
+                       const TS* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
+                       const void* saved, TS* dx, float* dG_P, float* dG_R, void* ws,
+                       hipStream_t s) {
+  const int m = sh->m, n = sh->n, b = sh->b, T = sh->T;
+  const int es = (int)sizeof(TS);
+  const bool mf = use_mfma(sh);
+  const BwdWs w = bwd_ws(sh);
+  const TS* U = at<TS>(saved, saved_U(sh));
+  const TS* Z = at<TS>(saved, saved_Z(sh));
+  TS* dS = at<TS>(ws, w.dS);
+  TS* dZ = at<TS>(ws, w.dZ);
+  TS* dV = at<TS>(ws, w.dV);
+  TS* dU = at<TS>(ws, w.dU);
+  float* part = at<float>(ws, w.part);
+  const long bb = (long)b * b;
+  hipError_t e;
+  mark(0, s);
+  // dS = dy[:, pi_R]
+  if ((e = launch_permute_cols(T, m, es, dy, perm_R, dS, s)) != hipSuccess) return dev_fail(e, "gather dy");
+  mark(1, s);
+  // dZ_i = dS_i G_Ri  (B operand G_Ri^T)
+  if ((e = nt<TS>(mf, m / b, T, b, b, dS, m, b, GT_R, b, bb, dZ, m, b, s)) != hipSuccess)
+    return dev_fail(e, "R-side blocks (bwd)");
+  mark(2, s);
+  // dG_Ri = dS_i^T Z_i
+  if ((e = tn<TS>(mf, m / b, b, T, dS, m, Z, m, dG_R, part, s)) != hipSuccess)
+    return dev_fail(e, "dG_R");
+  mark(3, s);
+  // dV = dZ W0f  (B operand W0f^T)
+  if ((e = nt<TS>(mf, 1, T, n, m, dZ, m, 0, W0fT, m, 0, dV, n, 0, s)) != hipSuccess)
+    return dev_fail(e, "W0 product (bwd)");
+  mark(4, s);
+  // dU_j = dV_j G_Pj
+  if ((e = nt<TS>(mf, n / b, T, b, b, dV, n, b, GT_P, b, bb, dU, n, b, s)) != hipSuccess)
+    return dev_fail(e, "P-side blocks (bwd)");
+  mark(5, s);
+  // dG_Pj = dV_j^T U_j
+  if ((e = tn<TS>(mf, n / b, b, T, dV, n, U, n, dG_P, part, s)) != hipSuccess)
+    return dev_fail(e, "dG_P");
+  mark(6, s);
+  // dx[:, pi_P[c]] = dU[:, c]  <=>  dx = dU[:, pi_P^{-1}]
+  if ((e = launch_permute_cols(T, n, es, dU, perm_P_inv, dx, s)) != hipSuccess)
+    return dev_fail(e, "scatter dx");
+  mark(7, s);
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t poetx_abi_version(void) { return POETX_ABI_VERSION; }
+
+const char* poetx_status_str(int32_t st) {
+  switch (st) {
+    case POETX_OK: return "POETX_OK";
+    case POETX_ERR_ARG: return "POETX_ERR_ARG";
+    case POETX_ERR_UNSUPPORTED: return "POETX_ERR_UNSUPPORTED";
+    case POETX_ERR_WORKSPACE: return "POETX_ERR_WORKSPACE";
+    case POETX_ERR_DEVICE: return "POETX_ERR_DEVICE";
+    default: return "POETX_UNKNOWN_STATUS";
+  }
+}
+
+const char* poetx_last_error(void) { return g_err; }
+
+size_t poetx_cnp_workspace_bytes(int32_t nblk, int32_t b, int32_t k, int32_t which, int32_t act) {
+  if (which != 0 && which != 1) return 0;
+  if (check_cnp_args("poetx_cnp_workspace_bytes", nblk, b, k, act) != POETX_OK) return 0;
+  return cnp_ws(nblk, b, k, which, act);
+}
+
+int32_t poetx_cnp_fwd(int32_t nblk, int32_t b, int32_t k, const float* theta, void* G, void* GT,
+                      int32_t g_dtype, void* ws, size_t ws_bytes, poetx_stream_t stream) {
+  const char* fn = "poetx_cnp_fwd";
+  int32_t st = check_cnp_args(fn, nblk, b, k, g_dtype);
+  if (st != POETX_OK) return st;
+  NEED_PTR(theta);
+  NEED_PTR(G);
+  OPT_PTR(GT);
+  const size_t need = cnp_ws(nblk, b, k, 0, g_dtype);
+  if (need) {
+    NEED_PTR(ws);
+    if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (cnp_uses_panel(b, g_dtype))
+    e = launch_cnp_panel_fwd(nblk, b, k, theta, (bf16*)G, (bf16*)GT, (bf16*)ws, s);
+  else if (g_dtype == POETX_F32)
+    e = launch_cnp_small_fwd<float>(nblk, b, k, theta, (float*)G, (float*)GT, s);
+  else
+    e = launch_cnp_small_fwd<bf16>(nblk, b, k, theta, (bf16*)G, (bf16*)GT, s);
+  if (e != hipSuccess) return dev_fail(e, fn);
+  return ok();
+}
+
+int32_t poetx_cnp_bwd(int32_t nblk, int32_t b, int32_t k, const float* theta, const float* dG,
+                      float* dtheta, int32_t accumulate, int32_t prec, void* ws,
+                      size_t ws_bytes, poetx_stream_t stream) {
+  const char* fn = "poetx_cnp_bwd";
+  const int32_t act = prec;
+  int32_t st = check_cnp_args(fn, nblk, b, k, act);
+  if (st != POETX_OK) return st;
+  NEED_PTR(theta);
+  NEED_PTR(dG);
+  NEED_PTR(dtheta);
+  const size_t need = cnp_ws(nblk, b, k, 1, act);
+  if (need) {
+    NEED_PTR(ws);
+    if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (cnp_uses_panel(b, act)) {
+    const size_t bb = (size_t)b * b;
+    bf16* Qg = (bf16*)ws;
+    bf16* F = at<bf16>(ws, align_up(nblk * bb * 2));
+    float* dQ = at<float>(ws, align_up(nblk * bb * 2) + align_up((size_t)k * nblk * bb * 2));
+    e = launch_cnp_panel_bwd(nblk, b, k, theta, dG, dtheta, accumulate, Qg, F, dQ, s);
+  } else {
+    e = launch_cnp_small_bwd(nblk, b, k, theta, dG, dtheta, accumulate, (float*)ws, s);
+  }
+  if (e != hipSuccess) return dev_fail(e, fn);
+  return ok();
+}
+
+int32_t poetx_fold_perm(int32_t m, int32_t n, int32_t dt, const void* W0, const int32_t* perm_R,
+                        const int32_t* perm_P, void* W0f, void* W0fT, int32_t* perm_R_inv,
+                        int32_t* perm_P_inv, poetx_stream_t stream) {
+  const char* fn = "poetx_fold_perm";
+  if (m < 1 || n < 1) return fail(POETX_ERR_ARG, "%s: m=%d n=%d must be >= 1", fn, m, n);
+  if (dt != POETX_F32 && dt != POETX_BF16) return fail(POETX_ERR_ARG, "%s: dtype %d", fn, dt);
+  NEED_PTR(W0);
+  NEED_PTR(perm_R);
+  NEED_PTR(perm_P);
+  NEED_PTR(W0f);
+  OPT_PTR(W0fT);
+  OPT_PTR(perm_R_inv);
+  OPT_PTR(perm_P_inv);
+  hipError_t e = launch_fold(m, n, (int)es_of(dt), W0, perm_R, perm_P, W0f, W0fT, perm_R_inv,
+                             perm_P_inv, (hipStream_t)stream);
+  if (e != hipSuccess) return dev_fail(e, fn);
+  return ok();
+}
+
+size_t poetx_workspace_bytes(const poetx_shape* sh, int32_t which) {
+  if (check_shape("poetx_workspace_bytes", sh) != POETX_OK) return 0;
+  if (which == 0) return fwd_ws(sh).total;
+  if (which == 1) return bwd_ws(sh).total;
+  return 0;
+}
+
+size_t poetx_saved_bytes(const poetx_shape* sh) {
+  if (check_shape("poetx_saved_bytes", sh) != POETX_OK) return 0;
+  return saved_total(sh);
+}
+
+int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P, const void* G_R,
+                        const void* W0f, const int32_t* perm_P, const int32_t* perm_R_inv,
+                        void* y, void* saved, void* ws, size_t ws_bytes, poetx_stream_t stream) {
+  const char* fn = "poetx_layer_fwd";
+  int32_t st = check_shape(fn, sh);
+  if (st != POETX_OK) return st;
+  NEED_PTR(x);
+  NEED_PTR(G_P);
+  NEED_PTR(G_R);
+  NEED_PTR(W0f);
+  NEED_PTR(perm_P);
+  NEED_PTR(perm_R_inv);
+  NEED_PTR(y);
+  NEED_PTR(saved);
+  NEED_PTR(ws);
+  const size_t need = fwd_ws(sh).total;
+  if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  if (sh->act == POETX_BF16)
+    return layer_fwd_impl<bf16>(sh, (const bf16*)x, (const bf16*)G_P, (const bf16*)G_R,
+                                (const bf16*)W0f, perm_P, perm_R_inv, (bf16*)y, saved, ws, s);
+  return layer_fwd_impl<float>(sh, (const float*)x, (const float*)G_P, (const float*)G_R,
+                               (const float*)W0f, perm_P, perm_R_inv, (float*)y, saved, ws, s);
+}
+
+int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P, const void* GT_R,
+                        const void* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
+                        const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
+                        size_t ws_bytes, poetx_stream_t stream) {
+  const char* fn = "poetx_layer_bwd";
+  int32_t st = check_shape(fn, sh);
+  if (st != POETX_OK) return st;
+  NEED_PTR(dy);
+  NEED_PTR(GT_P);
+  NEED_PTR(GT_R);
+  NEED_PTR(W0fT);
+  NEED_PTR(perm_P_inv);
+  NEED_PTR(perm_R);
+  NEED_PTR(saved);
+  NEED_PTR(dx);
+  NEED_PTR(dG_P);
+  NEED_PTR(dG_R);
+  NEED_PTR(ws);
+  const size_t need = bwd_ws(sh).total;
+  if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  if (sh->act == POETX_BF16)
+    return layer_bwd_impl<bf16>(sh, (const bf16*)dy, (const bf16*)GT_P, (const bf16*)GT_R,
+                                (const bf16*)W0fT, perm_P_inv, perm_R, saved, (bf16*)dx, dG_P,
+                                dG_R, ws, s);
+  return layer_bwd_impl<float>(sh, (const float*)dy, (const float*)GT_P, (const float*)GT_R,
+                               (const float*)W0fT, perm_P_inv, perm_R, saved, (float*)dx, dG_P,
+                               dG_R, ws, s);
+}
+
+}  // extern "C"
+
+extern "C" int32_t poetx_set_stage_events(void* const* events, int32_t count) {
+  if (!events) {
+    g_stage_on = 0;
+    return ok();
+  }
+  if (count < 8) return fail(POETX_ERR_ARG, "poetx_set_stage_events: count=%d < 8", count);
+  for (int i = 0; i < 8; ++i) {
+    if (!events[i]) return fail(POETX_ERR_ARG, "poetx_set_stage_events: null event %d", i);
+    g_stage_ev[i] = (hipEvent_t)events[i];
+  }
+  g_stage_on = 1;
+  return ok();
+}

@@ -1,0 +1,346 @@
+// Cayley-Neumann parameterization on bf16 MFMA, b in {64, 128, 256, 512}
+// ("POET-X ...", technical summary 2.4: Q held on-chip, higher powers and the
+// sum formed in one pass, the backward likewise fused).
+//
+// The pages keep Q and Q^2 in shared memory and form Q^3, Q^4 and the sum.
+// Here the series is evaluated in Horner form, which needs only Q on chip:
+//   G = sum_p c_p Q^p,  c = (1, 2, ..., 2, 1)
+//     = I + U_0,  U_k = Q,  U_p = 2Q + Q U_{p+1}   (p = k-1..0)
+// Every step is a LEFT multiplication by Q, so each column panel of U evolves
+// on its own: one workgroup owns a 32-column panel of one block, keeps Q in
+// LDS (b <= 256: 135 KB of the CU's 160 KB) and the panel in registers, and
+// runs all k steps without leaving the CU.  k products of b x b x 32 each:
+// 2 k b^3 flops per block, as for the power form.
+//
+// Backward (D = dL/dG, w_p = c_p (-1)^{p-1}, using Q^T = -Q):
+//   F_k = w_{k+1} D,  F_a = w_{a+1} D + F_{a+1} Q      -> row-local; its
+//       transpose F_a^T = w_{a+1} D^T - Q F_{a+1}^T is the same left-Horner
+//       on column panels of D^T (phase 1, stores F_a - w_{a+1} D in bf16)
+//   Y_k = F_k,        Y_a = F_a + Q Y_{a+1},  gQ = Y_0   -> column-local
+//       (phase 2, writes gQ in fp32)
+//   dtheta = triu1(gQ - gQ^T)                           (phase 3, pack)
+// 2 k products per block: 4 k b^3 flops.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16.  Operand layout (lane l of 64):
+//   A 32x16: A[l%32][8*(l/32) + i], i < 8      B 16x32: B[8*(l/32) + i][l%32]
+//   D 32x32: acc[r] = D[8*(r/4) + 4*(l/32) + r%4][l%32]
+#include "kernels.h"
+
+namespace poetx {
+
+namespace {
+
+constexpr int PW = 32;        // panel width (columns per workgroup)
+constexpr int PAD = 8;        // LDS row padding (bf16) -> conflict-free b128 reads
+constexpr int NT = 512;       // threads per workgroup (8 waves: one CU, latency hiding)
+constexpr int NWAVE = NT / 64;
+
+enum { MODE_FWD = 0, MODE_BWD1 = 1, MODE_BWD2 = 2 };
+
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); }
+
+// Qg[blk] = Q as bf16, one thread per packed parameter (coalesced reads),
+// plus the zero diagonal
+__global__ void k_unpack_q(int b, const float* __restrict__ theta, bf16* __restrict__ Qg) {
+  const int blk = blockIdx.y;
+  const int tb = b * (b - 1) / 2;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  bf16* q = Qg + (long)blk * b * b;
+  if (t < b) q[(long)t * b + t] = 0;
+  if (t >= tb) return;
+  int i, j;
+  tri_rc(t, b, i, j);
+  const float v = theta[(long)blk * tb + t];
+  q[(long)i * b + j] = f2bf(v);
+  q[(long)j * b + i] = f2bf(-v);
+}
+
+// the same into a padded LDS tile (row pitch qp), by the whole workgroup.
+// One workgroup runs per CU, so the block's parameters are fetched with
+// every 16-byte load in flight at once, then scattered: four consecutive
+// packed entries share a row except where a row ends.
+template <int B, int NTH>
+__device__ __forceinline__ void unpack_to_lds(const float* __restrict__ th, bf16* Qs, int qp) {
+  constexpr int TB = B * (B - 1) / 2;   // a multiple of 4 for b % 8 == 0
+  constexpr int NV = TB / 4;
+  constexpr int PER = (NV + NTH - 1) / NTH;
+  const float4* th4 = reinterpret_cast<const float4*>(th);
+  float4 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int q = u * NTH + threadIdx.x;
+    v[u] = q < NV ? th4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int i = threadIdx.x; i < B; i += NTH) Qs[i * qp + i] = 0;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int q = u * NTH + threadIdx.x;
+    if (q < NV) {
+      int i, j;
+      tri_rc(4 * q, B, i, j);
+      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        Qs[i * qp + j] = f2bf(e[c]);
+        Qs[j * qp + i] = f2bf(-e[c]);
+        if (++j == B) {
+          ++i;
+          j = i + 1;
+        }
+      }
+    }
+  }
+}
+
+template <int B, bool QLDS, int MODE>
+__global__ __launch_bounds__(NT, 1) void k_cnp_panel(int k, const float* __restrict__ theta,
+                                                  const bf16* __restrict__ Qg,
+                                                  const float* __restrict__ D,
+                                                  bf16* __restrict__ out_bf, bf16* __restrict__ out_bfT,
+                                                  float* __restrict__ out_f) {
+  constexpr int QP = B + PAD;
+  constexpr int RT = B / 32;                        // 32-row tiles in a block
+  constexpr int RTW = (RT + NWAVE - 1) / NWAVE;     // row tiles per wave
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* Xs = reinterpret_cast<bf16*>(smem);         // [PW][QP]: X^T
+  bf16* Qs = Xs + PW * QP;                          // [B][QP] (QLDS only)
+
+  const int J0 = blockIdx.x * PW;
+  const int blk = blockIdx.y;
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int col = lane % 32;
+  const long boff = (long)blk * B * B;
+  const bf16* Qb = Qg + boff;
+  const float* Db = D ? D + boff : nullptr;
+  const float* th = theta + (long)blk * (B * (B - 1) / 2);
+
+  if constexpr (QLDS) unpack_to_lds<B, NT>(th, Qs, QP);
+
+  // fixed part of the per-step addend, in accumulator layout
+  float base[RTW][16];
+  f32x16_t X[RTW];
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    const int rt = wave + t * NWAVE;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float bv = 0.f;
+      if (rt < RT) {
+        const int row = rt * 32 + acc_row(r, lane);
+        if (MODE == MODE_FWD) bv = skew_at_nb(th, row, J0 + col, B);     // Q[row][J0+c]
+        else if (MODE == MODE_BWD1) bv = Db[(long)(J0 + col) * B + row];  // D^T[row][c]
+        else bv = Db[(long)row * B + J0 + col];                          // D[row][J0+c]
+      }
+      base[t][r] = bv;
+      // initial state: U_k = Q (forward), w_{k+1} D^T or w_{k+1} D (backward)
+      X[t][r] = (MODE == MODE_FWD) ? bv : cnp_wcoef(k + 1, k) * bv;
+    }
+  }
+
+  auto store_xs = [&]() {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int rt = wave + t * NWAVE;
+      if (rt < RT) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int row = rt * 32 + acc_row(r, lane);  // rows row, row+1
+          *reinterpret_cast<uint32_t*>(Xs + col * QP + row) = pack2bf(X[t][r], X[t][r + 1]);
+        }
+      }
+    }
+  };
+  store_xs();
+  __syncthreads();
+
+  for (int step = k - 1; step >= 0; --step) {
+    // phase 2 adds F_step - w D: load it before the product so it arrives meanwhile
+    float fadd[RTW][16];
+    if constexpr (MODE == MODE_BWD2) {
+      const bf16* F = out_bf + ((long)step * gridDim.y + blk) * B * B;
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) {
+        const int rt = min(wave + t * NWAVE, RT - 1);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fadd[t][r] = bf2f(F[(long)(rt * 32 + acc_row(r, lane)) * B + J0 + col]);
+      }
+    }
+    // P = Q * X over the panel
+    f32x16_t P[RTW];
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) P[t] = (f32x16_t){};
+    if (wave < RT) {  // waves beyond the block's row tiles only join the barriers
+      // operand fragments double-buffered: the reads for k0+16 are issued
+      // before the MFMAs of k0
+      uint4 bq[2], aq[2][RTW];
+      auto fetch = [&](int k0, int s) {
+        const int kk = k0 + 8 * (lane / 32);
+        bq[s] = *reinterpret_cast<const uint4*>(Xs + col * QP + kk);
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) {
+          const int arow = min(wave + t * NWAVE, RT - 1) * 32 + (lane % 32);
+          if constexpr (QLDS) aq[s][t] = *reinterpret_cast<const uint4*>(Qs + arow * QP + kk);
+          else aq[s][t] = *reinterpret_cast<const uint4*>(Qb + (long)arow * B + kk);
+        }
+      };
+      auto mma = [&](int s) {
+#pragma unroll
+        for (int t = 0; t < RTW; ++t)
+          if (wave + t * NWAVE < RT) P[t] = mfma32x32x16(as_bf16x8(aq[s][t]), as_bf16x8(bq[s]), P[t]);
+      };
+      fetch(0, 0);
+#pragma unroll 2
+      for (int k0 = 0; k0 < B; k0 += 32) {  // buffer indices stay compile-time
+        fetch(k0 + 16, 1);
+        mma(0);
+        if (k0 + 32 < B) fetch(k0 + 32, 0);
+        mma(1);
+      }
+    }
+    __syncthreads();  // every wave finished reading Xs
+    const float wstep = (MODE == MODE_FWD) ? cnp_coef(step + 1, k) : cnp_wcoef(step + 1, k);
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int rt = wave + t * NWAVE;
+      if (rt >= RT) continue;
+      if (MODE == MODE_FWD) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) X[t][r] = wstep * base[t][r] + P[t][r];
+      } else if (MODE == MODE_BWD1) {
+        // F_step - w D = -(Q F_{step+1}^T) transposed: store rows J0+c
+        bf16* F = out_bf + ((long)step * gridDim.y + blk) * B * B;
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const int row = rt * 32 + acc_row(r, lane);
+          uint2 pk;
+          pk.x = pack2bf(-P[t][r], -P[t][r + 1]);
+          pk.y = pack2bf(-P[t][r + 2], -P[t][r + 3]);
+          *reinterpret_cast<uint2*>(F + (long)(J0 + col) * B + row) = pk;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) X[t][r] = wstep * base[t][r] - P[t][r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) X[t][r] = wstep * base[t][r] + fadd[t][r] + P[t][r];
+      }
+    }
+    if (step > 0) {
+      store_xs();
+      __syncthreads();
+    }
+  }
+
+  // outputs
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) {
+    const int rt = wave + t * NWAVE;
+    if (rt >= RT) continue;
+    if (MODE == MODE_FWD) {
+      bf16* G = out_bf + boff;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rt * 32 + acc_row(r, lane);
+        X[t][r] += (row == J0 + col) ? 1.f : 0.f;
+        G[(long)row * B + J0 + col] = f2bf(X[t][r]);
+      }
+      if (out_bfT) {
+        bf16* GT = out_bfT + boff;
+#pragma unroll
+        for (int r = 0; r < 16; r += 4) {
+          const int row = rt * 32 + acc_row(r, lane);
+          uint2 pk;
+          pk.x = pack2bf(X[t][r], X[t][r + 1]);
+          pk.y = pack2bf(X[t][r + 2], X[t][r + 3]);
+          *reinterpret_cast<uint2*>(GT + (long)(J0 + col) * B + row) = pk;
+        }
+      }
+    } else if (MODE == MODE_BWD2) {
+      float* dQ = out_f + boff;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = rt * 32 + acc_row(r, lane);
+        dQ[(long)row * B + J0 + col] = X[t][r];
+      }
+    }
+  }
+}
+
+// dtheta[t(i,j)] (+)= gQ[i][j] - gQ[j][i], one workgroup per (row i, block)
+__global__ void k_pack_skew(int b, const float* __restrict__ dQ, float* __restrict__ dtheta,
+                            int accumulate) {
+  const int i = blockIdx.x, blk = blockIdx.y;
+  const float* g = dQ + (long)blk * b * b;
+  float* dth = dtheta + (long)blk * (b * (b - 1) / 2) + tri_index(i, i + 1, b) - (i + 1);
+  for (int j = i + 1 + threadIdx.x; j < b; j += blockDim.x) {
+    float v = g[(long)i * b + j] - g[(long)j * b + i];
+    dth[j] = accumulate ? dth[j] + v : v;
+  }
+}
+
+template <int B, int MODE>
+hipError_t launch_panel(int nblk, int k, const float* theta, const bf16* Qg, const float* D,
+                        bf16* out_bf, bf16* out_bfT, float* out_f, hipStream_t s) {
+  constexpr bool QLDS = B <= 256;
+  constexpr size_t lds = (size_t)(PW + (QLDS ? B : 0)) * (B + PAD) * sizeof(bf16);
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = k_cnp_panel<B, QLDS, MODE>;
+  // the LDS opt-in is a host call; make it once per kernel, not per launch
+  static const hipError_t attr =
+      lds > 64 * 1024 ? hipFuncSetAttribute((const void*)kern,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                      : hipSuccess;
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL(kern, dim3(B / PW, nblk), dim3(NT), lds, s, k, theta, Qg, D, out_bf,
+                     out_bfT, out_f);
+  return hipGetLastError();
+}
+
+template <int MODE>
+hipError_t dispatch_panel(int nblk, int b, int k, const float* theta, const bf16* Qg,
+                          const float* D, bf16* out_bf, bf16* out_bfT, float* out_f,
+                          hipStream_t s) {
+  switch (b) {
+    case 64: return launch_panel<64, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
+    case 128: return launch_panel<128, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
+    case 256: return launch_panel<256, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
+    case 512: return launch_panel<512, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// blocks above 256 read Q from a bf16 copy in global memory; smaller ones
+// build it in LDS straight from theta
+hipError_t unpack(int nblk, int b, const float* theta, bf16* Qg, hipStream_t s) {
+  if (b <= 256) return hipSuccess;
+  const int tb = b * (b - 1) / 2;
+  hipLaunchKernelGGL(k_unpack_q, dim3((unsigned)((tb + 255) / 256), nblk), dim3(256), 0, s, b,
+                     theta, Qg);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_cnp_panel_fwd(int nblk, int b, int k, const float* theta, bf16* G, bf16* GT,
+                                bf16* ws_Q, hipStream_t s) {
+  hipError_t e = unpack(nblk, b, theta, ws_Q, s);
+  if (e != hipSuccess) return e;
+  return dispatch_panel<MODE_FWD>(nblk, b, k, theta, ws_Q, nullptr, G, GT, nullptr, s);
+}
+
+hipError_t launch_cnp_panel_bwd(int nblk, int b, int k, const float* theta, const float* dG,
+                                float* dtheta, int accumulate, bf16* ws_Q, bf16* ws_F,
+                                float* ws_dQ, hipStream_t s) {
+  hipError_t e = unpack(nblk, b, theta, ws_Q, s);
+  if (e != hipSuccess) return e;
+  if (k > 0) {
+    e = dispatch_panel<MODE_BWD1>(nblk, b, k, theta, ws_Q, dG, ws_F, nullptr, nullptr, s);
+    if (e != hipSuccess) return e;
+  }
+  e = dispatch_panel<MODE_BWD2>(nblk, b, k, theta, ws_Q, dG, ws_F, nullptr, ws_dQ, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pack_skew, dim3(b - 1, nblk), dim3(256), 0, s, b, ws_dQ, dtheta,
+                     accumulate);
+  return hipGetLastError();
+}
+
+}  // namespace poetx

@@ -1,0 +1,71 @@
+// Host-side launchers of the POET-X kernels (internal to libpoetx.so).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace poetx {
+
+// Coefficients of G = sum_p c_p Q^p = (I+Q)(I + ... + Q^k):
+// c_0 = 1, c_p = 2 for 1 <= p <= k, c_{k+1} = 1.
+__host__ __device__ inline float cnp_coef(int p, int k) {
+  if (p == 0 || p == k + 1) return 1.0f;
+  return 2.0f;
+}
+// Backward weights w_p = c_p (-1)^{p-1} (Q^T = -Q folds the transposes).
+__host__ __device__ inline float cnp_wcoef(int p, int k) {
+  return ((p - 1) & 1) ? -cnp_coef(p, k) : cnp_coef(p, k);
+}
+
+// ---- permutations (perm.hip) ------------------------------------------
+hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
+                       const int32_t* pP, void* W0f, void* W0fT, int32_t* pRinv,
+                       int32_t* pPinv, hipStream_t s);
+// out[r][c] = in[r][idx[c]] for r < rows, c < width; es = element bytes (2|4)
+hipError_t launch_permute_cols(int rows, int width, int es, const void* in,
+                               const int32_t* idx, void* out, hipStream_t s);
+
+// ---- portable tiled kernels (simple.hip) ----------------------------------
+// C[bt][i][j] = sum_k A[bt][i][k] * B[bt][j][k]       (row-major, fp32 accumulate)
+template <typename TS>
+hipError_t launch_simple_nt(int batch, int M, int N, int K, const TS* A, long lda,
+                            long sA, const TS* B, long ldb, long sB, TS* C, long ldc,
+                            long sC, hipStream_t s);
+// C[bt][i][j] = sum_k A[bt][k][i] * B[bt][k][j]       (float32 output)
+template <typename TS>
+hipError_t launch_simple_tn(int batch, int M, int N, int K, const TS* A, long lda,
+                            long sA, const TS* B, long ldb, long sB, float* C, long ldc,
+                            long sC, hipStream_t s);
+// Cayley-Neumann forward/backward for b <= 64: one workgroup per block, the
+// block resident in LDS, fp32 arithmetic.
+template <typename TS>
+hipError_t launch_cnp_small_fwd(int nblk, int b, int k, const float* theta, TS* G, TS* GT,
+                                hipStream_t s);
+hipError_t launch_cnp_small_bwd(int nblk, int b, int k, const float* theta, const float* dG,
+                                float* dtheta, int accumulate, float* ws_F, hipStream_t s);
+
+// ---- bf16 MFMA GEMMs (gemm_mfma.hip) --------------------------------------
+// usable when N % 64 == 0 and K % 64 == 0 (M any)
+bool mfma_nt_ok(int M, int N, int K);
+// C[bt] = A[bt] B[bt]^T; A [M][K] (row pitch lda), B [N][K] (ldb), C [M][N] (ldc)
+hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
+                          const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
+                          hipStream_t s);
+// out[bt][r][c] = sum_t A[t][bt*sA + r] B[t][bt*sB + c], D x D per batch,
+// D in {64, 128, 256, 512}; partials: tn_partial_bytes(batch, D, T) bytes
+hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long sA, const bf16* B,
+                          long ldb, long sB, float* out, float* partials, hipStream_t s);
+size_t tn_partial_bytes(int batch, int D, int T);
+
+// ---- MFMA Cayley-Neumann panels (cnp_mfma.hip), bf16, b in {64..512} -------
+// ws_Q: nblk*b*b bf16 scratch holding the unpacked skew blocks.
+hipError_t launch_cnp_panel_fwd(int nblk, int b, int k, const float* theta, bf16* G,
+                                bf16* GT, bf16* ws_Q, hipStream_t s);
+// ws_Q as above; ws_F: k*nblk*b*b bf16; ws_dQ: nblk*b*b float.
+hipError_t launch_cnp_panel_bwd(int nblk, int b, int k, const float* theta, const float* dG,
+                                float* dtheta, int accumulate, bf16* ws_Q, bf16* ws_F,
+                                float* ws_dQ, hipStream_t s);
+
+}  // namespace poetx

@@ -1,0 +1,149 @@
+// Permutations as index maps ("POET-X ...", technical summary 2.2: data are
+// reordered by index instead of multiplying by permutation matrices; two of
+// the four forward permutations fold into the fixed weight).
+//
+// A column permutation of a token-major [rows][width] tensor gathers inside
+// each row.  Rows up to 64 KB are staged in LDS with coalesced 16-byte loads,
+// gathered from LDS and written back with coalesced 16-byte stores, so HBM
+// sees one streaming read and one streaming write per element.
+#include "kernels.h"
+
+namespace poetx {
+
+namespace {
+
+constexpr int PERM_THREADS = 256;
+constexpr int PERM_LDS_MAX = 64 * 1024;
+
+template <typename E>
+__device__ __forceinline__ void copy_row_to_lds(E* lds, const E* __restrict__ src, int width,
+                                                bool vec) {
+  if (vec) {
+    const int nv = width * (int)sizeof(E) / 16;
+    typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+    u32x4* l4 = reinterpret_cast<u32x4*>(lds);
+    for (int v = threadIdx.x; v < nv; v += blockDim.x) l4[v] = __builtin_nontemporal_load(s4 + v);
+  } else {
+    for (int c = threadIdx.x; c < width; c += blockDim.x) lds[c] = src[c];
+  }
+}
+
+// out[r][c] = in[rmap ? rmap[r] : r][idx[c]]
+template <typename E>
+__global__ __launch_bounds__(PERM_THREADS) void k_permute_rows_lds(
+    int rows, int width, const E* __restrict__ in, const int32_t* __restrict__ rmap,
+    const int32_t* __restrict__ idx, E* __restrict__ out, int vec) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  E* row = reinterpret_cast<E*>(smem);
+  constexpr int PER = 16 / sizeof(E);  // elements per 16-byte store
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+    const long src = rmap ? (long)rmap[r] : (long)r;
+    copy_row_to_lds(row, in + src * width, width, vec);
+    __syncthreads();
+    E* dst = out + (long)r * width;
+    if (vec) {
+      const int nv = width / PER;
+      for (int v = threadIdx.x; v < nv; v += blockDim.x) {
+        E tmp[PER];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) tmp[e] = row[idx[v * PER + e]];
+        uint4 pk;
+        __builtin_memcpy(&pk, tmp, 16);
+        reinterpret_cast<uint4*>(dst)[v] = pk;
+      }
+    } else {
+      for (int c = threadIdx.x; c < width; c += blockDim.x) dst[c] = row[idx[c]];
+    }
+    __syncthreads();
+  }
+}
+
+// rows too wide for LDS: gather straight from global memory
+template <typename E>
+__global__ __launch_bounds__(PERM_THREADS) void k_permute_rows_direct(
+    int rows, int width, const E* __restrict__ in, const int32_t* __restrict__ rmap,
+    const int32_t* __restrict__ idx, E* __restrict__ out) {
+  for (int r = blockIdx.x; r < rows; r += gridDim.x) {
+    const E* src = in + (rmap ? (long)rmap[r] : (long)r) * width;
+    E* dst = out + (long)r * width;
+    for (int c = threadIdx.x; c < width; c += blockDim.x) dst[c] = src[idx[c]];
+  }
+}
+
+// out[j][i] = in[i][j], in: [m][n]
+template <typename E>
+__global__ __launch_bounds__(256) void k_transpose(int m, int n, const E* __restrict__ in,
+                                                   E* __restrict__ out) {
+  __shared__ E tile[32][33];
+  const int tx = threadIdx.x % 32, ty = threadIdx.x / 32;  // 32 x 8
+  const int i0 = blockIdx.y * 32, j0 = blockIdx.x * 32;
+  for (int y = ty; y < 32; y += 8) {
+    int i = i0 + y, j = j0 + tx;
+    if (i < m && j < n) tile[y][tx] = in[(long)i * n + j];
+  }
+  __syncthreads();
+  for (int y = ty; y < 32; y += 8) {
+    int j = j0 + y, i = i0 + tx;
+    if (i < m && j < n) out[(long)j * m + i] = tile[tx][y];
+  }
+}
+
+__global__ void k_inverse_perm(int n, const int32_t* __restrict__ p, int32_t* __restrict__ inv) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) inv[p[i]] = i;
+}
+
+template <typename E>
+hipError_t permute_impl(int rows, int width, const void* in, const int32_t* rmap,
+                        const int32_t* idx, void* out, hipStream_t s) {
+  const size_t bytes = (size_t)width * sizeof(E);
+  const int grid = rows < 65536 ? rows : 65536;
+  if (bytes <= PERM_LDS_MAX) {
+    int vec = (bytes % 16 == 0) && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    hipLaunchKernelGGL(k_permute_rows_lds<E>, dim3(grid), dim3(PERM_THREADS), bytes, s, rows,
+                       width, (const E*)in, rmap, idx, (E*)out, vec);
+  } else {
+    hipLaunchKernelGGL(k_permute_rows_direct<E>, dim3(grid), dim3(PERM_THREADS), 0, s, rows,
+                       width, (const E*)in, rmap, idx, (E*)out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_permute_cols(int rows, int width, int es, const void* in, const int32_t* idx,
+                               void* out, hipStream_t s) {
+  if (rows <= 0 || width <= 0) return hipSuccess;
+  if (es == 2) return permute_impl<uint16_t>(rows, width, in, nullptr, idx, out, s);
+  return permute_impl<uint32_t>(rows, width, in, nullptr, idx, out, s);
+}
+
+hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
+                       const int32_t* pP, void* W0f, void* W0fT, int32_t* pRinv,
+                       int32_t* pPinv, hipStream_t s) {
+  hipError_t e = es == 2 ? permute_impl<uint16_t>(m, n, W0, pR, pP, W0f, s)
+                         : permute_impl<uint32_t>(m, n, W0, pR, pP, W0f, s);
+  if (e != hipSuccess) return e;
+  if (W0fT) {
+    dim3 grid((n + 31) / 32, (m + 31) / 32);
+    if (es == 2)
+      hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, m, n,
+                         (const uint16_t*)W0f, (uint16_t*)W0fT);
+    else
+      hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(256), 0, s, m, n,
+                         (const uint32_t*)W0f, (uint32_t*)W0fT);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (pRinv) {
+    hipLaunchKernelGGL(k_inverse_perm, dim3((m + 255) / 256), dim3(256), 0, s, m, pR, pRinv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (pPinv) {
+    hipLaunchKernelGGL(k_inverse_perm, dim3((n + 255) / 256), dim3(256), 0, s, n, pP, pPinv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace poetx

@@ -1,0 +1,137 @@
+"""A POET-X layer driven through libpoetx.so.
+
+`POETXLayer` owns every device buffer of one layer shape (the folded weight,
+the orthogonal blocks, saved activations, workspaces, gradients) and runs the
+forward pass, the backward pass, or one whole training step of the layer
+through the C ABI on the current HIP stream.  `POETXLinear` wraps it as a
+torch.nn.Module whose packed parameters get gradients through autograd.
+PyTorch supplies device memory and streams only.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import poetx as P
+
+_DT = {P.F32: torch.float32, P.BF16: torch.bfloat16}
+
+
+def _bytes(n: int, device) -> torch.Tensor:
+    return torch.empty(max(int(n), 16), dtype=torch.uint8, device=device)
+
+
+class POETXLayer:
+    """Buffers and calls for one (m, n, b, k, T, dtype) layer."""
+
+    def __init__(self, m: int, n: int, b: int, k: int, T: int, act: int, device="cuda"):
+        self.m, self.n, self.b, self.k, self.T, self.act = m, n, b, k, T, act
+        self.sh = P.shape(m, n, b, k, T, act)
+        dt = self.dtype = _DT[act]
+        dev = self.device = torch.device(device)
+        nP, nR = n // b, m // b
+        self.nP, self.nR = nP, nR
+        e = lambda *s, d=dt: torch.empty(*s, dtype=d, device=dev)
+        self.W0f, self.W0fT = e(m, n), e(n, m)
+        self.perm_P = e(n, d=torch.int32)
+        self.perm_R = e(m, d=torch.int32)
+        self.perm_P_inv = e(n, d=torch.int32)
+        self.perm_R_inv = e(m, d=torch.int32)
+        self.G_P, self.GT_P = e(nP, b, b), e(nP, b, b)
+        self.G_R, self.GT_R = e(nR, b, b), e(nR, b, b)
+        self.y = e(T, m)
+        self.dx = e(T, n)
+        self.dG_P = e(nP, b, b, d=torch.float32)
+        self.dG_R = e(nR, b, b, d=torch.float32)
+        tb = b * (b - 1) // 2
+        self.dtheta_P = e(nP, tb, d=torch.float32)
+        self.dtheta_R = e(nR, tb, d=torch.float32)
+        self.saved = _bytes(P.poetx_saved_bytes(self.sh), dev)
+        self.ws_fwd = _bytes(P.poetx_workspace_bytes(self.sh, 0), dev)
+        self.ws_bwd = _bytes(P.poetx_workspace_bytes(self.sh, 1), dev)
+        nmax = max(nP, nR)
+        self.ws_cnp_fwd = _bytes(P.poetx_cnp_workspace_bytes(nmax, b, k, 0, act), dev)
+        self.ws_cnp_bwd = _bytes(P.poetx_cnp_workspace_bytes(nmax, b, k, 1, act), dev)
+        self.theta_P = self.theta_R = None
+
+    # -- set-up, once per inner loop (untimed) --------------------------------
+    def load(self, W0: torch.Tensor, theta_P: torch.Tensor, theta_R: torch.Tensor,
+             perm_P: torch.Tensor, perm_R: torch.Tensor) -> None:
+        self.perm_P.copy_(perm_P)
+        self.perm_R.copy_(perm_R)
+        W0 = W0.to(self.device, self.dtype).contiguous()
+        P.poetx_fold_perm(W0, self.perm_R, self.perm_P, self.W0f, self.W0fT,
+                          self.perm_R_inv, self.perm_P_inv)
+        self.theta_P = theta_P.to(self.device, torch.float32).contiguous()
+        self.theta_R = theta_R.to(self.device, torch.float32).contiguous()
+
+    # -- the hot path ---------------------------------------------------------
+    def cnp(self) -> None:
+        P.poetx_cnp_fwd(self.theta_P, self.b, self.k, self.G_P, self.GT_P, self.ws_cnp_fwd)
+        P.poetx_cnp_fwd(self.theta_R, self.b, self.k, self.G_R, self.GT_R, self.ws_cnp_fwd)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        self.cnp()
+        P.poetx_layer_fwd(self.sh, x, self.G_P, self.G_R, self.W0f, self.perm_P,
+                          self.perm_R_inv, self.y, self.saved, self.ws_fwd)
+        return self.y
+
+    def backward(self, dy: torch.Tensor):
+        P.poetx_layer_bwd(self.sh, dy, self.GT_P, self.GT_R, self.W0fT, self.perm_P_inv,
+                          self.perm_R, self.saved, self.dx, self.dG_P, self.dG_R, self.ws_bwd)
+        P.poetx_cnp_bwd(self.theta_R, self.dG_R, self.b, self.k, self.dtheta_R, self.act,
+                        ws=self.ws_cnp_bwd)
+        P.poetx_cnp_bwd(self.theta_P, self.dG_P, self.b, self.k, self.dtheta_P, self.act,
+                        ws=self.ws_cnp_bwd)
+        return self.dx, self.dtheta_P, self.dtheta_R
+
+    def step(self, x: torch.Tensor, dy: torch.Tensor):
+        """One training step of the layer: every stage of the hot path."""
+        self.forward(x)
+        return self.backward(dy)
+
+
+class _POETXFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, theta_P, theta_R, layer: POETXLayer):
+        layer.theta_P = theta_P.detach().contiguous()
+        layer.theta_R = theta_R.detach().contiguous()
+        y = layer.forward(x.contiguous()).clone()
+        ctx.layer = layer
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        L = ctx.layer
+        dx, dP, dR = L.backward(dy.to(L.dtype).contiguous())
+        return dx.clone(), dP.clone(), dR.clone(), None
+
+
+class POETXLinear(torch.nn.Module):
+    """y = x (R W0 P)^T with a fixed random W0 and CNP-parameterized R, P.
+
+    theta_P / theta_R start at 0 (R = P = I, the layer equals W0).
+    `start_inner_loop()` draws new permutations and folds them into W0.
+    One module serves one token count T (its workspaces are sized for it).
+    """
+
+    def __init__(self, n: int, m: int, b: int, k: int, T: int, dtype=torch.bfloat16,
+                 seed: int = 0, device="cuda"):
+        super().__init__()
+        act = P.act_of(dtype)
+        g = torch.Generator().manual_seed(seed)
+        self.register_buffer("W0", (torch.randn(m, n, generator=g) / n ** 0.5).to(dtype).to(device))
+        tb = b * (b - 1) // 2
+        self.theta_P = torch.nn.Parameter(torch.zeros(n // b, tb, device=device))
+        self.theta_R = torch.nn.Parameter(torch.zeros(m // b, tb, device=device))
+        self._layer = POETXLayer(m, n, b, k, T, act, device)
+        self._gen = g
+        self.start_inner_loop()
+
+    def start_inner_loop(self) -> None:
+        pP = torch.randperm(self._layer.n, generator=self._gen).to(torch.int32)
+        pR = torch.randperm(self._layer.m, generator=self._gen).to(torch.int32)
+        self._layer.load(self.W0, self.theta_P.detach(), self.theta_R.detach(),
+                         pP.to(self.W0.device), pR.to(self.W0.device))
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        return _POETXFn.apply(x, self.theta_P, self.theta_R, self._layer)

@@ -1,0 +1,115 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before anything reaches a device.  CPU only: every
+call here fails validation, so no kernel is launched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from orthogonal_reparameterized_02_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "poetx.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libpoetx.so not built")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(poetx_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    L = _lib.lib()
+    syms = declared_symbols()
+    assert len(syms) >= 11
+    for s in syms:
+        assert hasattr(L, s), s
+        assert s in _lib.SIGNATURES, s
+    assert set(_lib.SIGNATURES) == set(syms)
+    assert L.poetx_abi_version() == 1
+
+
+def test_status_strings():
+    L = _lib.lib()
+    assert L.poetx_status_str(0) == b"POETX_OK"
+    assert L.poetx_status_str(3) == b"POETX_ERR_WORKSPACE"
+    assert L.poetx_status_str(99) == b"POETX_UNKNOWN_STATUS"
+
+
+FAKE = C.c_void_p(0x10000)      # aligned, never dereferenced: every call fails first
+MISALIGNED = C.c_void_p(0x10002)
+
+
+def test_cnp_argument_errors():
+    L = _lib.lib()
+    ok_args = lambda **kw: dict(dict(nblk=4, b=32, k=4, theta=FAKE, G=FAKE, GT=None, dt=1,
+                                     ws=None, wsb=0, s=None), **kw)
+    call = lambda a: L.poetx_cnp_fwd(a["nblk"], a["b"], a["k"], a["theta"], a["G"], a["GT"],
+                                     a["dt"], a["ws"], a["wsb"], a["s"])
+    assert call(ok_args(b=7)) == 1
+    assert call(ok_args(nblk=0)) == 1
+    assert call(ok_args(k=-1)) == 1
+    assert call(ok_args(k=9)) == 1
+    assert call(ok_args(theta=None)) == 1
+    assert b"theta" in L.poetx_last_error()
+    assert call(ok_args(G=MISALIGNED)) == 1
+    assert b"aligned" in L.poetx_last_error()
+    assert call(ok_args(dt=0, b=128)) == 2          # float32 blocks above 64
+    assert call(ok_args(dt=5)) == 1
+    # bf16 b=256 needs a workspace
+    need = L.poetx_cnp_workspace_bytes(4, 256, 4, 0, 1)
+    assert need >= 4 * 256 * 256 * 2
+    assert call(ok_args(b=256, ws=FAKE, wsb=need - 1)) == 3
+    assert L.poetx_cnp_bwd(4, 256, 4, FAKE, FAKE, FAKE, 0, 1, FAKE,
+                           L.poetx_cnp_workspace_bytes(4, 256, 4, 1, 1) - 1, None) == 3
+    assert L.poetx_cnp_bwd(4, 32, 4, FAKE, None, FAKE, 0, 0, FAKE, 1 << 20, None) == 1
+    assert L.poetx_cnp_workspace_bytes(4, 7, 4, 0, 1) == 0
+
+
+def test_layer_argument_errors():
+    L = _lib.lib()
+    good = _lib.Shape(4096, 4096, 256, 4, 8192, 1)
+    assert L.poetx_workspace_bytes(C.byref(good), 0) > 0
+    assert L.poetx_workspace_bytes(C.byref(good), 1) > 0
+    assert L.poetx_saved_bytes(C.byref(good)) >= 8192 * (4096 + 4096) * 2
+    bad = [
+        _lib.Shape(4000, 4096, 256, 4, 8192, 1),   # m % b
+        _lib.Shape(4096, 4096, 100, 4, 8192, 1),   # b
+        _lib.Shape(4096, 4096, 256, 4, 0, 1),      # T
+        _lib.Shape(4096, 4096, 256, -1, 8192, 1),  # k
+        _lib.Shape(4096, 4096, 256, 4, 8192, 3),   # dtype
+    ]
+    for sh in bad:
+        assert L.poetx_workspace_bytes(C.byref(sh), 0) == 0
+        assert L.poetx_saved_bytes(C.byref(sh)) == 0
+        st = L.poetx_layer_fwd(C.byref(sh), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                               FAKE, 1 << 40, None)
+        assert st == 1, L.poetx_last_error()
+    f32big = _lib.Shape(4096, 4096, 256, 4, 64, 0)
+    assert L.poetx_layer_fwd(C.byref(f32big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, 1 << 40, None) == 2
+    # workspace too small
+    need = L.poetx_workspace_bytes(C.byref(good), 0)
+    assert L.poetx_layer_fwd(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, need - 1, None) == 3
+    need = L.poetx_workspace_bytes(C.byref(good), 1)
+    assert L.poetx_layer_bwd(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, FAKE, need - 1, None) == 3
+    # null pointers are named
+    assert L.poetx_layer_bwd(C.byref(good), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, FAKE, need, None) == 1
+    assert b"GT_R" in L.poetx_last_error()
+    assert L.poetx_fold_perm(0, 4, 1, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == 1
+    assert L.poetx_fold_perm(4, 4, 1, FAKE, None, FAKE, FAKE, None, None, None, None) == 1
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    from orthogonal_reparameterized_02_amd import poetx as P
+    th = torch.zeros(2, 32 * 31 // 2)
+    G = torch.zeros(2, 32, 32)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        P.poetx_cnp_fwd(th, 32, 4, G)
