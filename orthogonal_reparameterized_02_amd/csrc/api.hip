@@ -192,6 +192,16 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
   if ((e = nt<TS>(mf, n / b, T, b, b, U, n, b, G_P, b, bb, V, n, b, s)) != hipSuccess)
     return dev_fail(e, "P-side blocks");
   mark(2, s);
+  if constexpr (sizeof(TS) == 2) {
+    if (mf && mfma_nt_block_ok(T, m, n, b)) {
+      // Z = V W0f^T and, per 256-column tile, S_i = Z_i G_Ri^T in one kernel
+      if ((e = launch_mfma_nt_block(T, m, n, V, n, W0f, n, Z, m, G_R, S, m, s)) != hipSuccess)
+        return dev_fail(e, "W0 product + R-side blocks");
+      mark(3, s);
+      mark(4, s);
+      goto scatter;
+    }
+  }
   // Z = V W0f^T
   if ((e = nt<TS>(mf, 1, T, m, n, V, n, 0, W0f, n, 0, Z, m, 0, s)) != hipSuccess)
     return dev_fail(e, "W0 product");
@@ -200,6 +210,7 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
   if ((e = nt<TS>(mf, m / b, T, b, b, Z, m, b, G_R, b, bb, S, m, b, s)) != hipSuccess)
     return dev_fail(e, "R-side blocks");
   mark(4, s);
+scatter:
   // y[:, pi_R[c]] = S[:, c]  <=>  y = S[:, pi_R^{-1}]
   if ((e = launch_permute_cols(T, m, es, S, perm_R_inv, y, s)) != hipSuccess)
     return dev_fail(e, "scatter y");
@@ -237,13 +248,27 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   if ((e = tn<TS>(mf, m / b, b, T, dS, m, Z, m, dG_R, part, s)) != hipSuccess)
     return dev_fail(e, "dG_R");
   mark(3, s);
-  // dV = dZ W0f  (B operand W0f^T)
-  if ((e = nt<TS>(mf, 1, T, n, m, dZ, m, 0, W0fT, m, 0, dV, n, 0, s)) != hipSuccess)
-    return dev_fail(e, "W0 product (bwd)");
-  mark(4, s);
-  // dU_j = dV_j G_Pj
-  if ((e = nt<TS>(mf, n / b, T, b, b, dV, n, b, GT_P, b, bb, dU, n, b, s)) != hipSuccess)
-    return dev_fail(e, "P-side blocks (bwd)");
+  {
+    bool fused = false;
+    if constexpr (sizeof(TS) == 2) {
+      if (mf && mfma_nt_block_ok(T, n, m, b)) {
+        // dV = dZ W0f and, per 256-column tile, dU_j = dV_j G_Pj in one kernel
+        if ((e = launch_mfma_nt_block(T, n, m, dZ, m, W0fT, m, dV, n, GT_P, dU, n, s)) != hipSuccess)
+          return dev_fail(e, "W0 product + P-side blocks (bwd)");
+        mark(4, s);
+        fused = true;
+      }
+    }
+    if (!fused) {
+      // dV = dZ W0f  (B operand W0f^T)
+      if ((e = nt<TS>(mf, 1, T, n, m, dZ, m, 0, W0fT, m, 0, dV, n, 0, s)) != hipSuccess)
+        return dev_fail(e, "W0 product (bwd)");
+      mark(4, s);
+      // dU_j = dV_j G_Pj
+      if ((e = nt<TS>(mf, n / b, T, b, b, dV, n, b, GT_P, b, bb, dU, n, b, s)) != hipSuccess)
+        return dev_fail(e, "P-side blocks (bwd)");
+    }
+  }
   mark(5, s);
   // dG_Pj = dV_j^T U_j
   if ((e = tn<TS>(mf, n / b, b, T, dV, n, U, n, dG_P, part, s)) != hipSuccess)

@@ -55,40 +55,24 @@ __global__ void k_unpack_q(int b, const float* __restrict__ theta, bf16* __restr
   q[(long)j * b + i] = f2bf(-v);
 }
 
-// the same into a padded LDS tile (row pitch qp), by the whole workgroup.
-// One workgroup runs per CU, so the block's parameters are fetched with
-// every 16-byte load in flight at once, then scattered: four consecutive
-// packed entries share a row except where a row ends.
+// Copy the unpacked block Qg [B][B] into the padded LDS tile (row pitch
+// qp).  One workgroup runs per CU, so every 16-byte load is put in flight
+// before the first LDS write.
 template <int B, int NTH>
-__device__ __forceinline__ void unpack_to_lds(const float* __restrict__ th, bf16* Qs, int qp) {
-  constexpr int TB = B * (B - 1) / 2;   // a multiple of 4 for b % 8 == 0
-  constexpr int NV = TB / 4;
-  constexpr int PER = (NV + NTH - 1) / NTH;
-  const float4* th4 = reinterpret_cast<const float4*>(th);
-  float4 v[PER];
+__device__ __forceinline__ void q_to_lds(const bf16* __restrict__ Qb, bf16* Qs, int qp) {
+  constexpr int VPR = B / 8;                 // 16-byte vectors per row
+  constexpr int PER = B * VPR / NTH;         // vectors per thread
+  static_assert(B * VPR % NTH == 0, "tile split");
+  uint4 v[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int q = u * NTH + threadIdx.x;
-    v[u] = q < NV ? th4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    v[u] = *reinterpret_cast<const uint4*>(Qb + (q / VPR) * B + (q % VPR) * 8);
   }
-  for (int i = threadIdx.x; i < B; i += NTH) Qs[i * qp + i] = 0;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int q = u * NTH + threadIdx.x;
-    if (q < NV) {
-      int i, j;
-      tri_rc(4 * q, B, i, j);
-      const float e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        Qs[i * qp + j] = f2bf(e[c]);
-        Qs[j * qp + i] = f2bf(-e[c]);
-        if (++j == B) {
-          ++i;
-          j = i + 1;
-        }
-      }
-    }
+    *reinterpret_cast<uint4*>(Qs + (q / VPR) * qp + (q % VPR) * 8) = v[u];
   }
 }
 
@@ -114,7 +98,7 @@ __global__ __launch_bounds__(NT, 1) void k_cnp_panel(int k, const float* __restr
   const float* Db = D ? D + boff : nullptr;
   const float* th = theta + (long)blk * (B * (B - 1) / 2);
 
-  if constexpr (QLDS) unpack_to_lds<B, NT>(th, Qs, QP);
+  if constexpr (QLDS) q_to_lds<B, NT>(Qb, Qs, QP);
 
   // fixed part of the per-step addend, in accumulator layout
   float base[RTW][16];
@@ -308,10 +292,9 @@ hipError_t dispatch_panel(int nblk, int b, int k, const float* theta, const bf16
   }
 }
 
-// blocks above 256 read Q from a bf16 copy in global memory; smaller ones
-// build it in LDS straight from theta
+// every block size reads Q from this bf16 copy: blocks up to 256 stage it in
+// LDS, larger ones stream it through L2 as the MFMA A operand
 hipError_t unpack(int nblk, int b, const float* theta, bf16* Qg, hipStream_t s) {
-  if (b <= 256) return hipSuccess;
   const int tb = b * (b - 1) / 2;
   hipLaunchKernelGGL(k_unpack_q, dim3((unsigned)((tb + 255) / 256), nblk), dim3(256), 0, s, b,
                      theta, Qg);

@@ -7,16 +7,22 @@
 //             bf16 in, fp32 accumulate, bf16 out.  Serves Z = V W0f^T,
 //             dV = dZ W0f (B = W0f^T), and every per-token block product
 //             (A = a b-column slice of the activations, B = G or G^T).
+//             Optional block epilogue: when the output tile's 256 columns
+//             are exactly one b = 256 orthogonal block g, the tile also
+//             computes E = C_tile Bk_g^T (K = 256) from LDS and stores it, so
+//             Z -> S_i = Z_i G_Ri^T and dV -> dU_j = dV_j G_Pj leave the CU
+//             without a second pass over HBM.
 //   gemm_tn:  P[s][bt] = sum over a token range of A^T B, A [T][*] and
 //             B [T][*] token-major, fp32 partial sums (dG = dS^T Z and
 //             dG_P = dV^T U); a fixed-order reduction over s follows.
 //
-// One workgroup = 4 wave64s in a 2 x 2 grid, tile BM x BN, K in slabs of 64
-// staged through LDS (double buffered, one barrier per slab).  LDS rows hold
-// 64 bf16 (128 B) as eight 16-byte chunks, chunk c of row r stored at
-// position c ^ ((r ^ r/8) & 7): MFMA operand reads (16 rows, one chunk) and
-// both the row-wise (NT) and the transposing (TN) tile writes are free of
-// bank conflicts.
+// Workgroups of WM x WN wave64s; tile BM x BN; K in slabs of 64 staged
+// through LDS (double buffered, one barrier per slab).  The 256 x 256 tile
+// runs 8 waves (two per SIMD) with 128 x 64 per wave, so one wave's LDS and
+// global-memory waits overlap the other's MFMAs.  LDS rows hold 64 bf16
+// (128 B) as eight 16-byte chunks, chunk c of row r stored at position
+// c ^ ((r ^ r/8) & 7): MFMA operand reads (16 rows, one chunk) and both the
+// row-wise (NT) and the transposing (TN) tile writes avoid bank conflicts.
 // MFMA: v_mfma_f32_32x32x16_bf16; lane l holds A[l%32][8*(l/32)+i] and
 // B[8*(l/32)+i][l%32]; acc[r] = D[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include <algorithm>
@@ -29,7 +35,6 @@ namespace {
 
 constexpr int BK = 64;
 constexpr int ROWB = BK * 2;  // bytes per LDS row
-constexpr int NTHR = 256;
 
 __device__ __forceinline__ int lds_off(int r, int c) {
   return r * ROWB + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
@@ -39,37 +44,55 @@ __device__ __forceinline__ int acc_row(int r, int lane) {
   return 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 struct Cfg {
-  static constexpr int TM = BM / 2, TN = BN / 2;  // wave tile
+  static constexpr int NTH = 64 * WM * WN;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int FM = TM / 32, FN = TN / 32;
   static constexpr int A_BYTES = BM * ROWB;
   static constexpr int STAGE = (BM + BN) * ROWB;
   static constexpr int LDS = 2 * STAGE;
-  static_assert(FM >= 1 && FN >= 1, "tile too small");
+  static constexpr int RPP = NTH / 8;               // rows per load pass
+  static constexpr int PA = BM / RPP, PB = BN / RPP;
+  static_assert(FM >= 1 && FN >= 1 && PA >= 1 && PB >= 1, "tile too small");
 };
 
-// acc += A_slab(rows of this wave) * B_slab(rows of this wave)^T over BK
-template <int BM, int BN>
+template <int FM, int FN, int TM, int TN>
+__device__ __forceinline__ void frag_load(const char* __restrict__ As, const char* __restrict__ Bs,
+                                          bf16x8_t (&a)[FM], bf16x8_t (&b)[FN], int ks, int wm,
+                                          int wn, int lane) {
+  const int c = ks * 2 + lane / 32;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + lds_off(wm * TM + i * 32 + lane % 32, c)));
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    b[j] = as_bf16x8(*reinterpret_cast<const uint4*>(Bs + lds_off(wn * TN + j * 32 + lane % 32, c)));
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void frag_mma(const bf16x8_t (&a)[FM], const bf16x8_t (&b)[FN],
+                                         f32x16_t (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
+}
+
+// acc += A_slab(rows of this wave) * B_slab(rows of this wave)^T over BK;
+// the LDS reads of sub-step ks+1 are issued before the MFMAs of ks
+template <class C>
 __device__ __forceinline__ void mma_slab(const char* __restrict__ As, const char* __restrict__ Bs,
-                                         f32x16_t (&acc)[Cfg<BM, BN>::FM][Cfg<BM, BN>::FN],
-                                         int wm, int wn, int lane) {
-  using C = Cfg<BM, BN>;
-#pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    const int c = ks * 2 + lane / 32;
-    bf16x8_t a[C::FM], b[C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-      a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(As + lds_off(wm * C::TM + i * 32 + lane % 32, c)));
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      b[j] = as_bf16x8(*reinterpret_cast<const uint4*>(Bs + lds_off(wn * C::TN + j * 32 + lane % 32, c)));
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc[i][j] = mfma32x32x16(a[i], b[j], acc[i][j]);
-  }
+                                         f32x16_t (&acc)[C::FM][C::FN], int wm, int wn, int lane) {
+  bf16x8_t a0[C::FM], b0[C::FN], a1[C::FM], b1[C::FN];
+  frag_load<C::FM, C::FN, C::TM, C::TN>(As, Bs, a0, b0, 0, wm, wn, lane);
+  frag_load<C::FM, C::FN, C::TM, C::TN>(As, Bs, a1, b1, 1, wm, wn, lane);
+  frag_mma<C::FM, C::FN>(a0, b0, acc);
+  frag_load<C::FM, C::FN, C::TM, C::TN>(As, Bs, a0, b0, 2, wm, wn, lane);
+  frag_mma<C::FM, C::FN>(a1, b1, acc);
+  frag_load<C::FM, C::FN, C::TM, C::TN>(As, Bs, a1, b1, 3, wm, wn, lane);
+  frag_mma<C::FM, C::FN>(a0, b0, acc);
+  frag_mma<C::FM, C::FN>(a1, b1, acc);
 }
 
 // XCD-aware order: consecutive workgroup ids are dealt round-robin over the
@@ -88,15 +111,39 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tilesM, int tilesN,
   tn = in / gm;
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(NTHR, 1) void k_gemm_nt(int M, int N, int K, const bf16* __restrict__ A,
-                                                     long lda, long sA, const bf16* __restrict__ B,
-                                                     long ldb, long sB, bf16* __restrict__ Cm,
-                                                     long ldc, long sC, int tilesM, int tilesN) {
-  using C = Cfg<BM, BN>;
+// store a wave's accumulator tile as bf16: lanes l, l^1 exchange so each
+// stores two adjacent values (4 bytes).  Rows beyond M are skipped.
+template <int FM, int FN>
+__device__ __forceinline__ void store_acc_bf16(const f32x16_t (&acc)[FM][FN], bf16* __restrict__ C,
+                                               long ldc, int row0, int col0, int M, int N,
+                                               int lane) {
+  const bool odd = lane & 1;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+        const float got = __shfl_xor(odd ? v0 : v1, 1);
+        const int row = row0 + i * 32 + acc_row(r, lane) + (odd ? 1 : 0);
+        const int col = col0 + j * 32 + (lane % 32) - (odd ? 1 : 0);
+        const uint32_t pk = odd ? pack2bf(got, v1) : pack2bf(v0, got);
+        if (row < M && col < N) *reinterpret_cast<uint32_t*>(C + (long)row * ldc + col) = pk;
+      }
+}
+
+// EPI: 0 plain store; 1 also E = C_tile * Bk_g^T for the tile's block g
+// (requires BN == 256 == block size, N-tile index = block index)
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
+    int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const bf16* __restrict__ B,
+    long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN,
+    const bf16* __restrict__ Bk, bf16* __restrict__ E, long lde) {
+  using C = Cfg<BM, BN, WM, WN>;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int wm = wave / 2, wn = wave % 2;
+  const int wm = wave / WN, wn = wave % WN;
   int tm, tn;
   tile_of(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
@@ -105,29 +152,27 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_nt(int M, int N, int K, const 
   B += bt * sB;
   Cm += bt * sC;
 
-  // loader: 8 threads per 128-byte row slab, 32 rows per pass
-  constexpr int PA = BM / 32, PB = BN / 32;
   const int lr = tid / 8, lc = tid % 8;
-  uint4 ra0[PA], rb0[PB];
-  auto gload = [&](uint4 (&ra)[PA], uint4 (&rb)[PB], int k0) {
+  uint4 ra[C::PA], rb[C::PB];
+  auto gload = [&](int k0) {
 #pragma unroll
-    for (int p = 0; p < PA; ++p) {
-      const int row = m0 + p * 32 + lr;
+    for (int p = 0; p < C::PA; ++p) {
+      const int row = m0 + p * C::RPP + lr;
       ra[p] = row < M ? *reinterpret_cast<const uint4*>(A + row * lda + k0 + lc * 8) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < PB; ++p) {
-      const int row = n0 + p * 32 + lr;
+    for (int p = 0; p < C::PB; ++p) {
+      const int row = n0 + p * C::RPP + lr;
       rb[p] = row < N ? *reinterpret_cast<const uint4*>(B + row * ldb + k0 + lc * 8) : make_uint4(0, 0, 0, 0);
     }
   };
-  auto sstore = [&](const uint4 (&ra)[PA], const uint4 (&rb)[PB], int buf) {
+  auto sstore = [&](int buf) {
     char* As = smem + buf * C::STAGE;
     char* Bs = As + C::A_BYTES;
 #pragma unroll
-    for (int p = 0; p < PA; ++p) *reinterpret_cast<uint4*>(As + lds_off(p * 32 + lr, lc)) = ra[p];
+    for (int p = 0; p < C::PA; ++p) *reinterpret_cast<uint4*>(As + lds_off(p * C::RPP + lr, lc)) = ra[p];
 #pragma unroll
-    for (int p = 0; p < PB; ++p) *reinterpret_cast<uint4*>(Bs + lds_off(p * 32 + lr, lc)) = rb[p];
+    for (int p = 0; p < C::PB; ++p) *reinterpret_cast<uint4*>(Bs + lds_off(p * C::RPP + lr, lc)) = rb[p];
   };
 
   f32x16_t acc[C::FM][C::FN];
@@ -137,44 +182,89 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_nt(int M, int N, int K, const 
     for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x16_t){};
 
   const int nk = K / BK;
-  gload(ra0, rb0, 0);
-  sstore(ra0, rb0, 0);
+  gload(0);
+  sstore(0);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) gload(ra0, rb0, (kt + 1) * BK);
+    if (kt + 1 < nk) gload((kt + 1) * BK);
     const char* As = smem + cur * C::STAGE;
-    mma_slab<BM, BN>(As, As + C::A_BYTES, acc, wm, wn, lane);
-    if (kt + 1 < nk) sstore(ra0, rb0, cur ^ 1);
+    mma_slab<C>(As, As + C::A_BYTES, acc, wm, wn, lane);
+    if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
   }
 
-  // epilogue: pair lanes l, l^1 so each stores two adjacent bf16 (4 bytes)
-  const bool odd = lane & 1;
+  store_acc_bf16<C::FM, C::FN>(acc, Cm, ldc, m0 + wm * C::TM, n0 + wn * C::TN, M, N, lane);
+  if constexpr (EPI == 1) {
+    static_assert(BN == 256 && BN % BK == 0, "block epilogue needs a 256-column tile");
+    // C tile (bf16) -> LDS as four K-slabs of 64 columns, the A operand of
+    // E = C_tile Bk^T.  The main loop's stage buffers are free (last barrier).
+    constexpr int SLAB = BM * ROWB;
+    const bool odd = lane & 1;
 #pragma unroll
-  for (int i = 0; i < C::FM; ++i)
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
+      for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-        const float got = __shfl_xor(odd ? v0 : v1, 1);
-        const int row = m0 + wm * C::TM + i * 32 + acc_row(r, lane) + (odd ? 1 : 0);
-        const int col = n0 + wn * C::TN + j * 32 + (lane % 32) - (odd ? 1 : 0);
-        const uint32_t pk = odd ? pack2bf(got, v1) : pack2bf(v0, got);
-        if (row < M && col < N) *reinterpret_cast<uint32_t*>(Cm + row * ldc + col) = pk;
+        for (int r = 0; r < 16; r += 2) {
+          const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
+          const float got = __shfl_xor(odd ? v0 : v1, 1);
+          const int row = wm * C::TM + i * 32 + acc_row(r, lane) + (odd ? 1 : 0);
+          const int col = wn * C::TN + j * 32 + (lane % 32) - (odd ? 1 : 0);
+          const uint32_t pk = odd ? pack2bf(got, v1) : pack2bf(v0, got);
+          char* slab = smem + (col / BK) * SLAB;
+          const int cc = col % BK;
+          *reinterpret_cast<uint32_t*>(slab + lds_off(row, cc / 8) + (cc % 8) * 2) = pk;
+        }
+    __syncthreads();
+    // E[row][n] = sum_k Ct[row][k] Bk[g][n][k]: B fragments straight from
+    // global memory (the 128 KB block is shared by every tile of the block)
+    const bf16* Bg = Bk + (long)bt * 0 + (long)tn * 256 * 256;
+    f32x16_t e[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) e[i][j] = (f32x16_t){};
+    bf16x8_t bq[2][C::FN];
+    auto bfetch = [&](int k16, int s) {
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) {
+        const int n = wn * C::TN + j * 32 + lane % 32;
+        bq[s][j] = as_bf16x8(*reinterpret_cast<const uint4*>(Bg + (long)n * 256 + k16 * 16 + 8 * (lane / 32)));
       }
+    };
+    bfetch(0, 0);
+#pragma unroll
+    for (int k16 = 0; k16 < 16; k16 += 2) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int kk = k16 + h;
+        if (kk + 1 < 16) bfetch(kk + 1, h ^ 1);
+        const char* slab = smem + (kk / 4) * SLAB;
+        const int c = (kk % 4) * 2 + lane / 32;
+        bf16x8_t a[C::FM];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + lds_off(wm * C::TM + i * 32 + lane % 32, c)));
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) e[i][j] = mfma32x32x16(a[i], bq[h][j], e[i][j]);
+      }
+    }
+    store_acc_bf16<C::FM, C::FN>(e, E + (long)bt * 0, lde, m0 + wm * C::TM, n0 + wn * C::TN, M, N, lane);
+  }
 }
 
 // Partial token reduction: P[s][bt][r][c] = sum_{t in split s} A[t][r] B[t][c]
 // (A, B token-major, column offsets folded into the pointers per batch).
 template <int BT>
-__global__ __launch_bounds__(NTHR, 1) void k_gemm_tn(int T, int tsplit, int tiles1,
-                                                     const bf16* __restrict__ A, long lda, long sA,
-                                                     const bf16* __restrict__ B, long ldb, long sB,
-                                                     float* __restrict__ P, long ldp, long sP,
-                                                     long sS) {
-  using C = Cfg<BT, BT>;
+__global__ __launch_bounds__(256, 1) void k_gemm_tn(int T, int tsplit, int tiles1,
+                                                    const bf16* __restrict__ A, long lda, long sA,
+                                                    const bf16* __restrict__ B, long ldb, long sB,
+                                                    float* __restrict__ P, long ldp, long sP,
+                                                    long sS) {
+  using C = Cfg<BT, BT, 2, 2>;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
@@ -238,7 +328,7 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_tn(int T, int tsplit, int tile
       const int cur = kt & 1;
       if (kt + 1 < nk) gload(t_begin + (kt + 1) * BK);
       const char* As = smem + cur * C::STAGE;
-      mma_slab<BT, BT>(As, As + C::A_BYTES, acc, wm, wn, lane);
+      mma_slab<C>(As, As + C::A_BYTES, acc, wm, wn, lane);
       if (kt + 1 < nk) sstore(cur ^ 1);
       __syncthreads();
     }
@@ -252,6 +342,90 @@ __global__ __launch_bounds__(NTHR, 1) void k_gemm_tn(int T, int tsplit, int tile
         const int row = tm * BT + wm * C::TM + i * 32 + acc_row(r, lane);
         const int col = tn * BT + wn * C::TN + j * 32 + lane % 32;
         P[row * ldp + col] = acc[i][j][r];
+      }
+}
+
+// 8 x 8 bf16 transpose within one thread: in[t] holds tokens t, features
+// 0..7 (two per dword); out[f] holds feature f, tokens 0..7
+__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[t*4 + q]: features 2q, 2q+1
+  uint32_t* o = reinterpret_cast<uint32_t*>(out);              // o[f*4 + p]: tokens 2p, 2p+1
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t lo = w[(2 * p) * 4 + f / 2], hi = w[(2 * p + 1) * 4 + f / 2];
+      o[f * 4 + p] = __builtin_amdgcn_perm(hi, lo, (f & 1) ? 0x07060302u : 0x05040100u);
+    }
+}
+
+// Partial token reduction over a whole 256 x 256 block per workgroup, 8 waves
+// (128 x 64 each): P[s][bt] = sum_{t in split s} A_bt^T B_bt.  Each thread
+// loads an 8-token x 8-feature piece of A or B, transposes it in registers
+// and writes 16-byte LDS rows [feature][token].
+__global__ __launch_bounds__(512, 1) void k_gemm_tn256(int T, int tsplit, const bf16* __restrict__ A,
+                                                       long lda, long sA, const bf16* __restrict__ B,
+                                                       long ldb, long sB, float* __restrict__ P,
+                                                       int tiles1, long sP, long sS) {
+  using C = Cfg<256, 256, 2, 4>;
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int wm = wave / 4, wn = wave % 4;
+  const int tile = blockIdx.x;  // (tm, tn) of 256-blocks inside a D x D block
+  const int tm = tile / tiles1, tn = tile % tiles1;
+  const long bt = blockIdx.y;
+  const int s = blockIdx.z;
+  const int t_begin = s * tsplit, t_end = min(T, t_begin + tsplit);
+  // this thread's piece: operand (A: tid < 256), token group tg, feature group fg
+  const int opnd = tid / 256, piece = tid % 256;
+  const int tg = piece / 32, fg = piece % 32;
+  const bf16* src = opnd == 0 ? A + bt * sA + tm * 256 : B + bt * sB + tn * 256;
+  const long ld = opnd == 0 ? lda : ldb;
+  uint4 rin[8];
+  auto gload = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int t = t0 + tg * 8 + i;
+      rin[i] = t < t_end ? *reinterpret_cast<const uint4*>(src + (long)t * ld + fg * 8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint4 rt[8];
+    transpose8x8(rin, rt);
+    char* base = smem + buf * C::STAGE + opnd * C::A_BYTES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(base + lds_off(fg * 8 + i, tg)) = rt[i];
+  };
+  f32x16_t acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x16_t){};
+  const int nk = (t_end - t_begin + BK - 1) / BK;
+  if (nk > 0) {
+    gload(t_begin);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload(t_begin + (kt + 1) * BK);
+      const char* As = smem + cur * C::STAGE;
+      mma_slab<C>(As, As + C::A_BYTES, acc, wm, wn, lane);
+      if (kt + 1 < nk) sstore(cur ^ 1);
+      __syncthreads();
+    }
+  }
+  const int D = tiles1 * 256;
+  float* Pb = P + s * sS + bt * sP;
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = tm * 256 + wm * C::TM + i * 32 + acc_row(r, lane);
+        const int col = tn * 256 + wn * C::TN + j * 32 + lane % 32;
+        Pb[(long)row * D + col] = acc[i][j][r];
       }
 }
 
@@ -271,30 +445,33 @@ hipError_t set_lds(K kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN, int EPI>
 hipError_t nt_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA, const bf16* B,
-                     long ldb, long sB, bf16* C, long ldc, long sC, hipStream_t s) {
-  auto kern = k_gemm_nt<BM, BN>;
-  static const hipError_t attr = set_lds(kern, Cfg<BM, BN>::LDS);
+                     long ldb, long sB, bf16* C, long ldc, long sC, const bf16* Bk, bf16* E,
+                     long lde, hipStream_t s) {
+  using CF = Cfg<BM, BN, WM, WN>;
+  auto kern = k_gemm_nt<BM, BN, WM, WN, EPI>;
+  static const hipError_t attr = set_lds(kern, CF::LDS);
   if (attr != hipSuccess) return attr;
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-  constexpr int lds = Cfg<BM, BN>::LDS;
-  hipLaunchKernelGGL(kern, dim3(tilesM * tilesN, batch), dim3(NTHR), lds, s, M, N, K,
-                     A, lda, sA, B, ldb, sB, C, ldc, sC, tilesM, tilesN);
+  constexpr int lds = CF::LDS;
+  hipLaunchKernelGGL(kern, dim3(tilesM * tilesN, batch), dim3(CF::NTH), lds, s, M, N, K, A, lda,
+                     sA, B, ldb, sB, C, ldc, sC, tilesM, tilesN, Bk, E, lde);
   return hipGetLastError();
 }
 
 template <int BT>
 hipError_t tn_launch(int batch, int D, int T, int S, const bf16* A, long lda, long sA, const bf16* B,
                      long ldb, long sB, float* P, long ldp, long sP, long sS, hipStream_t s) {
+  using CF = Cfg<BT, BT, 2, 2>;
   auto kern = k_gemm_tn<BT>;
-  static const hipError_t attr = set_lds(kern, Cfg<BT, BT>::LDS);
+  static const hipError_t attr = set_lds(kern, CF::LDS);
   if (attr != hipSuccess) return attr;
   const int tiles1 = D / BT;
   const int tsplit = ((T + S - 1) / S + BK - 1) / BK * BK;
-  constexpr int lds = Cfg<BT, BT>::LDS;
-  hipLaunchKernelGGL(kern, dim3(tiles1 * tiles1, batch, S), dim3(NTHR), lds, s, T,
-                     tsplit, tiles1, A, lda, sA, B, ldb, sB, P, ldp, sP, sS);
+  constexpr int lds = CF::LDS;
+  hipLaunchKernelGGL(kern, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit, tiles1,
+                     A, lda, sA, B, ldb, sB, P, ldp, sP, sS);
   return hipGetLastError();
 }
 
@@ -309,17 +486,31 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
                           hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return (long)batch * ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (N % 256 == 0 && tiles(256, 256) >= NUM_CU)
-    return nt_launch<256, 256>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+    return nt_launch<256, 256, 2, 4, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
+                                        nullptr, nullptr, 0, s);
   if (N % 128 == 0 && tiles(256, 128) >= NUM_CU)
-    return nt_launch<256, 128>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+    return nt_launch<256, 128, 2, 2, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
+                                        nullptr, nullptr, 0, s);
   if (N % 128 == 0)
-    return nt_launch<128, 128>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
-  return nt_launch<128, 64>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+    return nt_launch<128, 128, 2, 2, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
+                                        nullptr, nullptr, 0, s);
+  return nt_launch<128, 64, 2, 2, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, nullptr,
+                                     nullptr, 0, s);
+}
+
+bool mfma_nt_block_ok(int M, int N, int K, int b) {
+  return b == 256 && N % 256 == 0 && K % BK == 0 && M > 0;
+}
+
+hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
+                                long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
+                                hipStream_t s) {
+  return nt_launch<256, 256, 2, 4, 1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
 }
 
 // splits of the token range for a D x D (per batch) reduction
 int tn_splits(int batch, int D, int T) {
-  const int BT = D >= 128 ? 128 : 64;
+  const int BT = D >= 256 ? 256 : (D >= 128 ? 128 : 64);
   const long tiles = (long)batch * (D / BT) * (D / BT);
   int S = (int)((NUM_CU + tiles - 1) / tiles);
   const int max_s = (T + 255) / 256;  // keep >= 256 tokens per split
@@ -338,10 +529,20 @@ hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long
   const long dd = (long)D * D;
   float* P = S > 1 ? partials : out;
   hipError_t e;
-  if (D == 64)
+  if (D >= 256) {
+    static const hipError_t attr = set_lds(k_gemm_tn256, Cfg<256, 256, 2, 4>::LDS);
+    if (attr != hipSuccess) return attr;
+    const int tiles1 = D / 256;
+    const int tsplit = ((T + S - 1) / S + BK - 1) / BK * BK;
+    constexpr int lds = Cfg<256, 256, 2, 4>::LDS;
+    hipLaunchKernelGGL(k_gemm_tn256, dim3(tiles1 * tiles1, batch, S), dim3(512), lds, s, T, tsplit,
+                       A, lda, sA, B, ldb, sB, P, tiles1, dd, dd * batch);
+    e = hipGetLastError();
+  } else if (D == 64) {
     e = tn_launch<64>(batch, D, T, S, A, lda, sA, B, ldb, sB, P, D, dd, dd * batch, s);
-  else
+  } else {
     e = tn_launch<128>(batch, D, T, S, A, lda, sA, B, ldb, sB, P, D, dd, dd * batch, s);
+  }
   if (e != hipSuccess || S == 1) return e;
   const long n = dd * batch;
   const int grid = (int)std::min<long>((n + 255) / 256, 4096);

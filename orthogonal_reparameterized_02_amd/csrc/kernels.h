@@ -53,6 +53,12 @@ bool mfma_nt_ok(int M, int N, int K);
 hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
                           hipStream_t s);
+// C = A B^T as above (one batch) and, per 256-column tile g of C (one
+// orthogonal block of size 256), E[:, g] = C[:, g] Bk[g]^T with Bk [N/256][256][256]
+bool mfma_nt_block_ok(int M, int N, int K, int b);
+hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
+                                long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
+                                hipStream_t s);
 // out[bt][r][c] = sum_t A[t][bt*sA + r] B[t][bt*sB + c], D x D per batch,
 // D in {64, 128, 256, 512}; partials: tn_partial_bytes(batch, D, T) bytes
 hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long sA, const bf16* B,
