@@ -160,6 +160,17 @@ hipError_t nt(bool mfma, int batch, int M, int N, int K, const TS* A, long lda, 
   return launch_simple_nt<TS>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
 }
 
+// Out[:, jb + n] = sum_k A[:, jb + k] Gb[j][n][k] for every block j (A and
+// Out row pitch `width`): the per-token block products
+template <typename TS>
+hipError_t blocks(bool mfma, int nblk, int T, int width, int b, const TS* A, const TS* Gb, TS* Out,
+                  hipStream_t s) {
+  if constexpr (sizeof(TS) == 2) {
+    if (mfma && mfma_blocks_ok(b)) return launch_mfma_blocks(nblk, T, width, b, A, Gb, Out, s);
+  }
+  return nt<TS>(mfma, nblk, T, b, b, A, width, b, Gb, b, (long)b * b, Out, width, b, s);
+}
+
 // out[bt] = A_bt^T B_bt over T tokens, D x D blocks at column offsets bt*D
 template <typename TS>
 hipError_t tn(bool mfma, int batch, int D, int T, const TS* A, long lda, const TS* B, long ldb,
@@ -189,7 +200,7 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
   if ((e = launch_permute_cols(T, n, es, x, perm_P, U, s)) != hipSuccess) return dev_fail(e, "gather x");
   mark(1, s);
   // V_j = U_j G_Pj^T
-  if ((e = nt<TS>(mf, n / b, T, b, b, U, n, b, G_P, b, bb, V, n, b, s)) != hipSuccess)
+  if ((e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
     return dev_fail(e, "P-side blocks");
   mark(2, s);
   if constexpr (sizeof(TS) == 2) {
@@ -207,7 +218,7 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
     return dev_fail(e, "W0 product");
   mark(3, s);
   // S_i = Z_i G_Ri^T
-  if ((e = nt<TS>(mf, m / b, T, b, b, Z, m, b, G_R, b, bb, S, m, b, s)) != hipSuccess)
+  if ((e = blocks<TS>(mf, m / b, T, m, b, Z, G_R, S, s)) != hipSuccess)
     return dev_fail(e, "R-side blocks");
   mark(4, s);
 scatter:
@@ -241,7 +252,7 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   if ((e = launch_permute_cols(T, m, es, dy, perm_R, dS, s)) != hipSuccess) return dev_fail(e, "gather dy");
   mark(1, s);
   // dZ_i = dS_i G_Ri  (B operand G_Ri^T)
-  if ((e = nt<TS>(mf, m / b, T, b, b, dS, m, b, GT_R, b, bb, dZ, m, b, s)) != hipSuccess)
+  if ((e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s)) != hipSuccess)
     return dev_fail(e, "R-side blocks (bwd)");
   mark(2, s);
   // dG_Ri = dS_i^T Z_i
@@ -265,7 +276,7 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
         return dev_fail(e, "W0 product (bwd)");
       mark(4, s);
       // dU_j = dV_j G_Pj
-      if ((e = nt<TS>(mf, n / b, T, b, b, dV, n, b, GT_P, b, bb, dU, n, b, s)) != hipSuccess)
+      if ((e = blocks<TS>(mf, n / b, T, n, b, dV, GT_P, dU, s)) != hipSuccess)
         return dev_fail(e, "P-side blocks (bwd)");
     }
   }

@@ -15,16 +15,24 @@ typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 __device__ __forceinline__ float bf2f(bf16 h) { return __uint_as_float((uint32_t)h << 16); }
 
 // float -> bfloat16, round to nearest, ties to even; NaN stays NaN.
-__device__ __forceinline__ bf16 f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16)(u >> 16);
-}
+// float -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32;
+// NaN stays NaN)
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw_t __attribute__((ext_vector_type(2)));
 
 // two floats -> two packed bf16 (lo in bits 0..15)
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_hw_t h = __builtin_convertvector((f32x2_hw_t){lo, hi}, bf16x2_hw_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &h, 4);
+  return u;
+}
+
+__device__ __forceinline__ bf16 f2bf(float f) {
+  const __bf16 h = (__bf16)f;
+  bf16 u;
+  __builtin_memcpy(&u, &h, 2);
+  return u;
 }
 
 // storage-type adaptors: the math is always fp32

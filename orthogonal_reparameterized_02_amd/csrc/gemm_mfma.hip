@@ -111,26 +111,55 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tilesM, int tilesN,
   tn = in / gm;
 }
 
-// store a wave's accumulator tile as bf16: lanes l, l^1 exchange so each
-// stores two adjacent values (4 bytes).  Rows beyond M are skipped.
+// Write a wave's accumulators as bf16 into LDS laid out as 64-column slabs
+// [col/64][row][64] (the MFMA operand layout).  Only fragments whose 32 rows
+// lie in [r_lo, r_hi) are written (partial staging); rbase and r_lo are
+// multiples of 32, so a fragment's swizzle keys are fixed per lane.  Each
+// lane packs its row pair (r, r+1) of one column; lanes l and l^1 swap
+// halves (DPP quad permute) so each writes two adjacent columns of one row.
 template <int FM, int FN>
-__device__ __forceinline__ void store_acc_bf16(const f32x16_t (&acc)[FM][FN], bf16* __restrict__ C,
-                                               long ldc, int row0, int col0, int M, int N,
-                                               int lane) {
-  const bool odd = lane & 1;
+__device__ __forceinline__ void acc_to_slabs(const f32x16_t (&acc)[FM][FN], char* lds, int slab_bytes,
+                                             int rbase, int cbase, int lane, int r_lo, int r_hi) {
+  const int odd = lane & 1;
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  const int rl = 4 * (lane >> 5) + odd;  // row within an 8-row group for r % 4 == 0
+  const int cl = (lane & 31) - odd;      // first column of the written pair
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int fr = rbase + i * 32 - r_lo;  // fragment's first row in the staging buffer
+    if (fr < 0 || fr >= r_hi - r_lo) continue;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FN; ++j) {
+      const int col = cbase + j * 32 + cl;
+      char* base = lds + (col >> 6) * slab_bytes + (fr + rl) * ROWB + (col & 7) * 2;
+      const int chx = ((col >> 3) & 7) ^ ((fr >> 3) & 4);
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-        const float got = __shfl_xor(odd ? v0 : v1, 1);
-        const int row = row0 + i * 32 + acc_row(r, lane) + (odd ? 1 : 0);
-        const int col = col0 + j * 32 + (lane % 32) - (odd ? 1 : 0);
-        const uint32_t pk = odd ? pack2bf(got, v1) : pack2bf(v0, got);
-        if (row < M && col < N) *reinterpret_cast<uint32_t*>(C + (long)row * ldc + col) = pk;
+        const uint32_t p = pack2bf(acc[i][j][r], acc[i][j][r + 1]);
+        const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0xB1, 0xF, 0xF, true);
+        const uint32_t v = __builtin_amdgcn_perm(q, p, sel);
+        const int key = chx ^ ((r & 3) + rl) ^ (r >> 2);
+        *reinterpret_cast<uint32_t*>(base + (8 * (r >> 2) + (r & 3)) * ROWB + (key << 4)) = v;
       }
+    }
+  }
+}
+
+// Copy ROWS x COLS bf16 from the slab layout to global memory with 16-byte
+// stores: consecutive lanes cover whole 128-byte row segments.
+template <int ROWS, int COLS, int NTH>
+__device__ __forceinline__ void slabs_to_global(const char* lds, bf16* __restrict__ C, long ldc,
+                                                int row0, int col0, int M, int N) {
+  constexpr int CHUNKS = ROWS * COLS / 8;
+  static_assert(CHUNKS % NTH == 0, "store split");
+#pragma unroll
+  for (int u = 0; u < CHUNKS / NTH; ++u) {
+    const int q = u * NTH + threadIdx.x;
+    const int s = q / (ROWS * 8), r = (q / 8) % ROWS, c = q % 8;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + s * ROWS * ROWB + lds_off(r, c));
+    const int row = row0 + r, col = col0 + s * BK + c * 8;
+    if (row < M && col < N) *reinterpret_cast<uint4*>(C + (long)row * ldc + col) = v;
+  }
 }
 
 // EPI: 0 plain store; 1 also E = C_tile * Bk_g^T for the tile's block g
@@ -194,65 +223,44 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
     __syncthreads();
   }
 
-  store_acc_bf16<C::FM, C::FN>(acc, Cm, ldc, m0 + wm * C::TM, n0 + wn * C::TN, M, N, lane);
+  // C tile -> LDS (64-column slabs; the main loop's last barrier freed the
+  // stage buffers) -> global with 16-byte stores over whole row segments
+  constexpr int SLAB = BM * ROWB;
+  static_assert(BN * SLAB / BK <= C::LDS, "staging fits in the stage buffers");
+  acc_to_slabs<C::FM, C::FN>(acc, smem, SLAB, wm * C::TM, wn * C::TN, lane, 0, BM);
+  __syncthreads();
+  slabs_to_global<BM, BN, C::NTH>(smem, Cm, ldc, m0, n0, M, N);
   if constexpr (EPI == 1) {
     static_assert(BN == 256 && BN % BK == 0, "block epilogue needs a 256-column tile");
-    // C tile (bf16) -> LDS as four K-slabs of 64 columns, the A operand of
-    // E = C_tile Bk^T.  The main loop's stage buffers are free (last barrier).
-    constexpr int SLAB = BM * ROWB;
-    const bool odd = lane & 1;
+    // the C tile now sits in LDS as four K-slabs of 64 columns: the A operand
+    // of E[row][n] = sum_k Ct[row][k] Bk[g][n][k].  The block's G slab
+    // [256 n][64 k] is staged in the 32 KB above it, the next slab's loads in
+    // flight during the current slab's MFMAs.
+    const bf16* Bg = Bk + (long)tn * 256 * 256;
+    char* Gs = smem + 4 * SLAB;
+    constexpr int GP = 256 / C::RPP;  // 16-byte loads per thread per slab
+    uint4 gq[GP];
+    auto gfetch = [&](int ks) {
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float v0 = acc[i][j][r], v1 = acc[i][j][r + 1];
-          const float got = __shfl_xor(odd ? v0 : v1, 1);
-          const int row = wm * C::TM + i * 32 + acc_row(r, lane) + (odd ? 1 : 0);
-          const int col = wn * C::TN + j * 32 + (lane % 32) - (odd ? 1 : 0);
-          const uint32_t pk = odd ? pack2bf(got, v1) : pack2bf(v0, got);
-          char* slab = smem + (col / BK) * SLAB;
-          const int cc = col % BK;
-          *reinterpret_cast<uint32_t*>(slab + lds_off(row, cc / 8) + (cc % 8) * 2) = pk;
-        }
-    __syncthreads();
-    // E[row][n] = sum_k Ct[row][k] Bk[g][n][k]: B fragments straight from
-    // global memory (the 128 KB block is shared by every tile of the block)
-    const bf16* Bg = Bk + (long)bt * 0 + (long)tn * 256 * 256;
-    f32x16_t e[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) e[i][j] = (f32x16_t){};
-    bf16x8_t bq[2][C::FN];
-    auto bfetch = [&](int k16, int s) {
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) {
-        const int n = wn * C::TN + j * 32 + lane % 32;
-        bq[s][j] = as_bf16x8(*reinterpret_cast<const uint4*>(Bg + (long)n * 256 + k16 * 16 + 8 * (lane / 32)));
-      }
+      for (int p = 0; p < GP; ++p)
+        gq[p] = *reinterpret_cast<const uint4*>(Bg + (long)(p * C::RPP + lr) * 256 + ks * BK + lc * 8);
     };
-    bfetch(0, 0);
 #pragma unroll
-    for (int k16 = 0; k16 < 16; k16 += 2) {
+    for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int kk = k16 + h;
-        if (kk + 1 < 16) bfetch(kk + 1, h ^ 1);
-        const char* slab = smem + (kk / 4) * SLAB;
-        const int c = (kk % 4) * 2 + lane / 32;
-        bf16x8_t a[C::FM];
+      for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x16_t){};
+    gfetch(0);
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-          a[i] = as_bf16x8(*reinterpret_cast<const uint4*>(slab + lds_off(wm * C::TM + i * 32 + lane % 32, c)));
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::FN; ++j) e[i][j] = mfma32x32x16(a[i], bq[h][j], e[i][j]);
-      }
+      for (int p = 0; p < GP; ++p) *reinterpret_cast<uint4*>(Gs + lds_off(p * C::RPP + lr, lc)) = gq[p];
+      __syncthreads();  // G slab visible
+      if (ks + 1 < 4) gfetch(ks + 1);
+      mma_slab<C>(smem + ks * SLAB, Gs, acc, wm, wn, lane);
+      __syncthreads();  // every wave is done with this G slab (and, at the end, the C tile)
     }
-    store_acc_bf16<C::FM, C::FN>(e, E + (long)bt * 0, lde, m0 + wm * C::TM, n0 + wn * C::TN, M, N, lane);
+    acc_to_slabs<C::FM, C::FN>(acc, smem, SLAB, wm * C::TM, wn * C::TN, lane, 0, BM);
+    __syncthreads();
+    slabs_to_global<BM, BN, C::NTH>(smem, E, lde, m0, n0, M, N);
   }
 }
 
@@ -343,6 +351,121 @@ __global__ __launch_bounds__(256, 1) void k_gemm_tn(int T, int tsplit, int tiles
         const int col = tn * BT + wn * C::TN + j * 32 + lane % 32;
         P[row * ldp + col] = acc[i][j][r];
       }
+}
+
+// Per-token block products, out[:, jB + n] = sum_k A[:, jB + k] G_j[n][k]
+// (V = U G_P^T, dZ = dS G_R with G := G_R^T).  One workgroup per (block j,
+// token range): G_j stays resident in LDS (B/64 K-slabs of [B][64]) while
+// token tiles of TOK rows stream through a double-buffered A slab, so the
+// operand pipeline never restarts between tiles and G_j is read once.
+template <int B, int TOK, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, int tiles_per_wg,
+                                                            const bf16* __restrict__ A,
+                                                            const bf16* __restrict__ G,
+                                                            bf16* __restrict__ Out) {
+  constexpr int NTH = 64 * WM * WN;
+  constexpr int TM = TOK / WM, TN = B / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int NS = B / BK;                    // K-slabs per token tile
+  constexpr int G_BYTES = B * B * 2;            // NS slabs of [B][64]
+  constexpr int A_SLAB = TOK * ROWB;
+  constexpr int RPP = NTH / 8;                  // rows per load pass
+  constexpr int PA = TOK / RPP, PG = B / RPP;
+  static_assert(PA >= 1 && PG >= 1 && FM >= 1 && FN >= 1, "shape");
+  using CF = Cfg<TOK, B, WM, WN>;
+  extern __shared__ __align__(16) char smem[];
+  char* Gs = smem;
+  char* As0 = smem + G_BYTES;
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int wm = wave / WN, wn = wave % WN;
+  const int lr = tid / 8, lc = tid % 8;
+  const int j = blockIdx.x;
+  const int tile0 = blockIdx.y * tiles_per_wg;
+  const int ntiles_total = (T + TOK - 1) / TOK;
+  const int ntiles = min(tiles_per_wg, ntiles_total - tile0);
+  if (ntiles <= 0) return;
+  const bf16* Aj = A + (long)j * B;
+  bf16* Oj = Out + (long)j * B;
+  // G_j -> LDS, every load in flight first
+  {
+    const bf16* Gj = G + (long)j * B * B;
+    uint4 gv[NS][PG];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int p = 0; p < PG; ++p)
+        gv[s][p] = *reinterpret_cast<const uint4*>(Gj + (long)(p * RPP + lr) * B + s * BK + lc * 8);
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int p = 0; p < PG; ++p)
+        *reinterpret_cast<uint4*>(Gs + s * B * ROWB + lds_off(p * RPP + lr, lc)) = gv[s][p];
+  }
+  // A slabs stream through a ring of four register sets: slab st+5 is
+  // requested as soon as slab st+1 leaves its set for LDS, so four slabs are
+  // in flight per workgroup while G_j stays resident
+  const int nsteps = ntiles * NS;
+  uint4 ra[4][PA];
+  auto aload = [&](uint4 (&r)[PA], int step) {  // step = tile * NS + slab
+    const int t0 = (tile0 + step / NS) * TOK, k0 = (step % NS) * BK;
+#pragma unroll
+    for (int p = 0; p < PA; ++p) {
+      const int row = t0 + p * RPP + lr;
+      r[p] = (step < nsteps && row < T)
+                 ? *reinterpret_cast<const uint4*>(Aj + (long)row * width + k0 + lc * 8)
+                 : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto astore = [&](const uint4 (&r)[PA], int buf) {
+    char* As = As0 + buf * A_SLAB;
+#pragma unroll
+    for (int p = 0; p < PA; ++p) *reinterpret_cast<uint4*>(As + lds_off(p * RPP + lr, lc)) = r[p];
+  };
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int jj = 0; jj < FN; ++jj) acc[i][jj] = (f32x16_t){};
+  aload(ra[0], 0);
+  aload(ra[1], 1);
+  aload(ra[2], 2);
+  aload(ra[3], 3);
+  astore(ra[0], 0);
+  aload(ra[0], 4);
+  __syncthreads();
+  for (int q = 0; q < nsteps; q += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int st = q + u;
+      if (st < nsteps) {
+        mma_slab<CF>(As0 + (u & 1) * A_SLAB, Gs + (st % NS) * B * ROWB, acc, wm, wn, lane);
+        if (st % NS == NS - 1) {  // token tile complete: store, restart the accumulators
+          // the A buffer just consumed stages the tile in passes of PROWS rows
+          // so the global stores cover whole 128-byte row segments
+          const int t0 = (tile0 + st / NS) * TOK;
+          constexpr int PROWS = A_SLAB / (B * 2);
+          char* stg = As0 + (u & 1) * A_SLAB;
+          __syncthreads();
+#pragma unroll
+          for (int p = 0; p < TOK / PROWS; ++p) {
+            acc_to_slabs<FM, FN>(acc, stg, PROWS * ROWB, wm * TM, wn * TN, lane, p * PROWS,
+                                 (p + 1) * PROWS);
+            __syncthreads();
+            slabs_to_global<PROWS, B, NTH>(stg, Oj, width, t0 + p * PROWS, 0, T, B);
+            __syncthreads();
+          }
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int jj = 0; jj < FN; ++jj) acc[i][jj] = (f32x16_t){};
+        }
+        if (st + 1 < nsteps) {
+          astore(ra[(u + 1) & 3], (u + 1) & 1);
+          aload(ra[(u + 1) & 3], st + 5);
+        }
+        __syncthreads();
+      }
+    }
+  }
 }
 
 // 8 x 8 bf16 transpose within one thread: in[t] holds tokens t, features
@@ -451,10 +574,12 @@ hipError_t nt_launch(int batch, int M, int N, int K, const bf16* A, long lda, lo
                      long lde, hipStream_t s) {
   using CF = Cfg<BM, BN, WM, WN>;
   auto kern = k_gemm_nt<BM, BN, WM, WN, EPI>;
-  static const hipError_t attr = set_lds(kern, CF::LDS);
+  // the block epilogue keeps the C tile (4 slabs) plus one 256 x 64 G slab
+  constexpr int lds = EPI == 1 ? (4 * BM + 256) * ROWB : CF::LDS;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-  constexpr int lds = CF::LDS;
   hipLaunchKernelGGL(kern, dim3(tilesM * tilesN, batch), dim3(CF::NTH), lds, s, M, N, K, A, lda,
                      sA, B, ldb, sB, C, ldc, sC, tilesM, tilesN, Bk, E, lde);
   return hipGetLastError();
@@ -506,6 +631,32 @@ hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, co
                                 long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
                                 hipStream_t s) {
   return nt_launch<256, 256, 2, 4, 1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+}
+
+bool mfma_blocks_ok(int b) { return b == 128 || b == 256; }
+
+template <int B, int TOK, int WM, int WN>
+hipError_t blocks_launch(int nblk, int T, int width, const bf16* A, const bf16* G, bf16* Out,
+                         hipStream_t s) {
+  auto kern = k_blocks<B, TOK, WM, WN>;
+  constexpr int lds = B * B * 2 + 2 * TOK * ROWB;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = set_lds(kern, lds);
+  if (attr != hipSuccess) return attr;
+  const int tiles = (T + TOK - 1) / TOK;
+  const int want = std::max(1, std::min(tiles, (NUM_CU + nblk - 1) / nblk));
+  const int per = (tiles + want - 1) / want;
+  const int splits = (tiles + per - 1) / per;
+  hipLaunchKernelGGL(kern, dim3(nblk, splits), dim3(64 * WM * WN), lds, s, T, width, per, A, G,
+                     Out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, const bf16* G,
+                              bf16* Out, hipStream_t s) {
+  if (b == 256) return blocks_launch<256, 128, 2, 4>(nblk, T, width, A, G, Out, s);
+  if (b == 128) return blocks_launch<128, 256, 4, 2>(nblk, T, width, A, G, Out, s);
+  return hipErrorInvalidValue;
 }
 
 // splits of the token range for a D x D (per batch) reduction

@@ -59,6 +59,11 @@ bool mfma_nt_block_ok(int M, int N, int K, int b);
 hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
                                 long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
                                 hipStream_t s);
+// per-token block products for b in {128, 256}:
+// Out[t][j b + n] = sum_k A[t][j b + k] G[j][n][k]  (A, Out row pitch `width`)
+bool mfma_blocks_ok(int b);
+hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, const bf16* G,
+                              bf16* Out, hipStream_t s);
 // out[bt][r][c] = sum_t A[t][bt*sA + r] B[t][bt*sB + c], D x D per batch,
 // D in {64, 128, 256, 512}; partials: tn_partial_bytes(batch, D, T) bytes
 hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long sA, const bf16* B,
