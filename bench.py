@@ -44,6 +44,10 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="after the timed steps, run a plain 1 GiB elementwise copy "
+                         "(torch.neg) three times: the reference kernel that calibrates "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
@@ -136,12 +140,24 @@ def main() -> int:
     stages["cnp_fwd"] = mean_ms(cnp_ev, 0, 1) * 1e3
     stages["cnp_bwd"] = mean_ms(cnp_ev, 2, 3) * 1e3
 
+    if args.copy_probe:
+        src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     T, m, n, b = cfg.T, cfg.m, cfg.n, cfg.b
     flops = step_flops(cfg)
     peak = PEAK_BF16_TFLOPS if act == P.BF16 else PEAK_FP32_TFLOPS
     tokens_per_s = T / (ms * 1e-3)
     dense_us = stages["dense_Z"]
-    dense_tflops = 2.0 * T * m * n / (dense_us * 1e-6) / 1e12
+    # b = 256 in bf16: the dense kernel also forms S = Z G_R^T per block in its
+    # epilogue (the library's fused path), 2 m b flops per token more
+    fused = act == P.BF16 and b == 256 and m % 256 == 0 and n % 64 == 0
+    dense_flops = 2.0 * T * m * n + (2.0 * T * m * b if fused else 0.0)
+    dense_tflops = dense_flops / (dense_us * 1e-6) / 1e12
     nblocks = cfg.n_P + cfg.n_R
 
     out = {
@@ -165,10 +181,12 @@ def main() -> int:
         "cnp_blocks_per_s": {"fwd": nblocks / (stages["cnp_fwd"] * 1e-6),
                              "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
-        "roofline": {"kernel": "dense_Z (Z = V W0f^T, bf16 MFMA GEMM)", "bound": "mfma",
-                     "achieved": dense_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": dense_tflops / peak, "traffic": None,
-                     "flops_per_launch": 2.0 * T * m * n, "avg_launch_us": dense_us},
+        "roofline": {"kernel": ("k_gemm_nt<256,256,2,4,1>: Z = V W0f^T with S = Z G_R^T "
+                                "in the epilogue" if fused else "k_gemm_nt: Z = V W0f^T"),
+                     "bound": "mfma", "achieved": dense_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": dense_tflops / peak,
+                     "traffic": measured_traffic(cfg.name) if fused else None,
+                     "flops_per_launch": dense_flops, "avg_launch_us": dense_us},
         "wall_s_timed": wall,
     }
 
@@ -176,6 +194,29 @@ def main() -> int:
         out["cpu_baseline"] = cpu_baseline(cfg, args.seed, min(args.cpu_sample_tokens, T))
     print(json.dumps(out), flush=True)
     return 0
+
+
+COPY_PROBE_BYTES = 1 << 30
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_nt_block_square_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "orthogonal_reparameterized_02_amd", "csrc", "gemm_mfma.hip")
+
+
+def measured_traffic(config_name: str):
+    """HBM bytes per launch of the dense kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summary, or None when that summary is absent, was
+    taken on another workload, or the kernel source has changed since."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            fields = dict(line.split(":", 1) for line in f if line.startswith("- ") and ":" in line)
+        fields = {k[2:].strip(): v.strip().strip("`") for k, v in fields.items()}
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if fields.get("source_sha256") != sha or fields.get("workload") != config_name:
+            return None
+        return float(fields["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(cfg, seed: int, ts: int) -> dict:
