@@ -181,7 +181,7 @@ def main() -> int:
         "cnp_blocks_per_s": {"fwd": nblocks / (stages["cnp_fwd"] * 1e-6),
                              "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
-        "roofline": {"kernel": ("k_gemm_nt<256,256,2,4,1>: Z = V W0f^T with S = Z G_R^T "
+        "roofline": {"kernel": ("k_nt4<1>: Z = V W0f^T with S = Z G_R^T "
                                 "in the epilogue" if fused else "k_gemm_nt: Z = V W0f^T"),
                      "bound": "mfma", "achieved": dense_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": dense_tflops / peak,

@@ -264,6 +264,151 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
   }
 }
 
+// 64-byte LDS rows (K slabs of 32): 16-byte chunk c of row r sits at slot
+// c ^ ((r/2 ^ r/8) & 3), so the 16 rows one MFMA operand read touches per
+// phase fall on distinct banks.
+__device__ __forceinline__ int off32(int r, int c) {
+  return r * 64 + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
+}
+
+// C = A B^T on a 256 x 256 tile with 4 waves (128 x 128 each, accumulators
+// in AGPRs).  K advances in slabs of 32 through NSTG = 4 LDS stages filled by
+// global_load_lds_dwordx4: the data go from L2 straight into LDS, so no
+// registers stage them and four slabs are in flight.  The DMA is issued from
+// inline asm (it has no register results) and its completion is tracked by
+// hand with vmcnt; the compiler therefore attaches no wait for it to the LDS
+// operand reads.  Each slab is two MFMA K-steps; the operand reads of the
+// next K-step are interleaved with the current MFMAs, and the one barrier per
+// slab sits between its two K-steps, where every wave has finished reading
+// the slab and the next one has landed.  EPI 1 adds the block epilogue of
+// k_gemm_nt.  Rows past M or N are clamped on load and masked on store.
+template <int EPI>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nt4(
+    int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const bf16* __restrict__ B,
+    long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN,
+    const bf16* __restrict__ Bk, bf16* __restrict__ E, long lde) {
+  constexpr int BM = 256, BN = 256, TM = 128, TN = 128, FM = 4, FN = 4, NTH = 256;
+  constexpr int NSTG = 4, SROW = 64, STG = (BM + BN) * SROW;  // 32 KB per stage
+  constexpr int SK = 32;                                      // K per slab
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int wm = wave / 2, wn = wave % 2;
+  int tm, tn;
+  tile_of(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const long bt = blockIdx.y;
+  A += bt * sA;
+  B += bt * sB;
+  Cm += bt * sC;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  // DMA instruction q of this wave fills 16 rows (1 KB) of a stage: rows
+  // 0..255 hold A, 256..511 hold B.  Lane l lands at byte 16 l of the block,
+  // i.e. row l/4, slot l%4, so it fetches the logical chunk stored there.
+  const bf16* src[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = (q * 4 + wave) * 16 + lane / 4;
+    const int c = (lane % 4) ^ (((r >> 1) ^ (r >> 3)) & 3);
+    if (q < 4) src[q] = A + (long)min(m0 + r, M - 1) * lda + c * 8;
+    else src[q] = B + (long)min(n0 + r - BM, N - 1) * ldb + c * 8;
+  }
+#define POETX_DMA(slab)                                                                        \
+  {                                                                                            \
+    const uint32_t sb_ = lds0 + ((slab) % NSTG) * STG;                                          \
+    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
+      const uint32_t m0v_ = __builtin_amdgcn_readfirstlane(sb_ + (q * 4 + wave) * 16 * SROW);  \
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v_),           \
+                   "v"(src[q] + (long)(slab) * SK)                                             \
+                   : "memory", "m0");                                                          \
+    }                                                                                          \
+  }
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16_t){};
+  bf16x8_t fa[2][FM], fb[2][FN];
+#define POETX_FLOAD(F, slab, ks)                                                               \
+  {                                                                                            \
+    const char* S_ = smem + ((slab) % NSTG) * STG;                                             \
+    const int c_ = (ks) * 2 + lane / 32;                                                       \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[F][i] = as_bf16x8(                       \
+        *reinterpret_cast<const uint4*>(S_ + off32(wm * TM + i * 32 + lane % 32, c_)));        \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[F][j] = as_bf16x8(                       \
+        *reinterpret_cast<const uint4*>(S_ + BM * SROW + off32(wn * TN + j * 32 + lane % 32, c_))); \
+  }
+#define POETX_MMA(F)                                                                           \
+  _Pragma("unroll") for (int i = 0; i < FM; ++i) _Pragma("unroll") for (int j = 0; j < FN; ++j) \
+      acc[i][j] = mfma32x32x16(fa[F][i], fb[F][j], acc[i][j]);                                 \
+  _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                              \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* one LDS read */                      \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* one MFMA */                          \
+  }                                                                                            \
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+  const int nk = K / SK;
+  POETX_DMA(0);
+  if (nk > 1) POETX_DMA(1);
+  if (nk > 2) POETX_DMA(2);
+  if (nk > 3) POETX_DMA(3);
+  // vmcnt counts this wave's DMA instructions, 8 per slab, completing in order
+  if (nk > 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if (nk > 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if (nk > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  POETX_FLOAD(0, 0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    POETX_FLOAD(1, kt, 1);
+    POETX_MMA(0);
+    // slab kt+1 has landed once at most the two slabs after it are pending;
+    // lgkmcnt(0): this wave's reads of slab kt are complete
+    const int ahead = min(2, nk - 2 - kt);
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (kt + NSTG < nk) POETX_DMA(kt + NSTG);  // into slab kt's stage, now free
+    if (kt + 1 < nk) POETX_FLOAD(0, kt + 1, 0);
+    POETX_MMA(1);
+  }
+#undef POETX_DMA
+#undef POETX_FLOAD
+#undef POETX_MMA
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  constexpr int SLAB = BM * ROWB;
+  acc_to_slabs<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane, 0, BM);
+  __syncthreads();
+  slabs_to_global<BM, BN, NTH>(smem, Cm, ldc, m0, n0, M, N);
+  if constexpr (EPI == 1) {
+    // as in k_gemm_nt: E = C_tile Bk_g^T from the staged tile, G slab by slab
+    using C = Cfg<BM, BN, 2, 2>;
+    const bf16* Bg = Bk + (long)tn * 256 * 256;
+    char* Gs = smem + 4 * SLAB;
+    constexpr int GP = 256 / C::RPP;
+    const int lr = tid / 8, lc = tid % 8;
+    uint4 gq[GP];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16_t){};
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int p = 0; p < GP; ++p)
+        gq[p] = *reinterpret_cast<const uint4*>(Bg + (long)(p * C::RPP + lr) * 256 + ks * BK + lc * 8);
+#pragma unroll
+      for (int p = 0; p < GP; ++p) *reinterpret_cast<uint4*>(Gs + lds_off(p * C::RPP + lr, lc)) = gq[p];
+      __syncthreads();  // G slab visible
+      mma_slab<C>(smem + ks * SLAB, Gs, acc, wm, wn, lane);
+      __syncthreads();  // every wave is done with this G slab (and, at the end, the C tile)
+    }
+    acc_to_slabs<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane, 0, BM);
+    __syncthreads();
+    slabs_to_global<BM, BN, NTH>(smem, E, lde, m0, n0, M, N);
+  }
+}
+
 // Partial token reduction: P[s][bt][r][c] = sum_{t in split s} A[t][r] B[t][c]
 // (A, B token-major, column offsets folded into the pointers per batch).
 template <int BT>
@@ -606,13 +751,30 @@ constexpr int NUM_CU = 256;
 
 bool mfma_nt_ok(int M, int N, int K) { return M > 0 && N % 64 == 0 && K % BK == 0; }
 
+// 4-wave 256 x 256 launcher; LDS: four 32 KB stages, or 160 KB for the
+// block epilogue's staged tile and G slab
+template <int EPI>
+hipError_t nt4_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
+                      const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC, const bf16* Bk,
+                      bf16* E, long lde, hipStream_t s) {
+  auto kern = k_nt4<EPI>;
+  constexpr int lds = EPI == 1 ? (4 * 256 + 256) * ROWB : 4 * 512 * 64;
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = set_lds(kern, lds);
+  if (attr != hipSuccess) return attr;
+  const int tM = (M + 255) / 256, tN = (N + 255) / 256;
+  hipLaunchKernelGGL(kern, dim3(tM * tN, batch), dim3(256), lds, s, M, N, K, A, lda, sA, B, ldb,
+                     sB, C, ldc, sC, tM, tN, Bk, E, lde);
+  return hipGetLastError();
+}
+
 hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
                           hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return (long)batch * ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   if (N % 256 == 0 && tiles(256, 256) >= NUM_CU)
-    return nt_launch<256, 256, 2, 4, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
-                                        nullptr, nullptr, 0, s);
+    return nt4_launch<0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, nullptr, nullptr, 0,
+                         s);
   if (N % 128 == 0 && tiles(256, 128) >= NUM_CU)
     return nt_launch<256, 128, 2, 2, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
                                         nullptr, nullptr, 0, s);
@@ -630,7 +792,7 @@ bool mfma_nt_block_ok(int M, int N, int K, int b) {
 hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
                                 long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
                                 hipStream_t s) {
-  return nt_launch<256, 256, 2, 4, 1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+  return nt4_launch<1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
 }
 
 bool mfma_blocks_ok(int b) { return b == 128 || b == 256; }
