@@ -277,10 +277,13 @@ __device__ __forceinline__ int off32(int r, int c) {
 // registers stage them and four slabs are in flight.  The DMA is issued from
 // inline asm (it has no register results) and its completion is tracked by
 // hand with vmcnt; the compiler therefore attaches no wait for it to the LDS
-// operand reads.  Each slab is two MFMA K-steps; the operand reads of the
-// next K-step are interleaved with the current MFMAs, and the one barrier per
-// slab sits between its two K-steps, where every wave has finished reading
-// the slab and the next one has landed.  EPI 1 adds the block epilogue of
+// operand reads.  Each slab is two MFMA K-steps.  With one wave per SIMD,
+// nothing else hides a stall of the MFMA pipe, so the issue order is fixed
+// by hand (sched_barrier): every pair of MFMAs is followed by one operand
+// read for the next K-step and, in the second K-step, by one of the wave's
+// eight DMA instructions for the slab four ahead.  The one barrier per slab
+// sits between its two K-steps, where every wave has finished reading the
+// slab and the next one has landed.  EPI 1 adds the block epilogue of
 // k_gemm_nt.  Rows past M or N are clamped on load and masked on store.
 template <int EPI>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nt4(
@@ -312,68 +315,79 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if (q < 4) src[q] = A + (long)min(m0 + r, M - 1) * lda + c * 8;
     else src[q] = B + (long)min(n0 + r - BM, N - 1) * ldb + c * 8;
   }
-#define POETX_DMA(slab)                                                                        \
+  // DMA instruction q of this wave: slab `from` into the stage of slab `slot`
+#define POETX_DMA1(slot, from, q)                                                              \
   {                                                                                            \
-    const uint32_t sb_ = lds0 + ((slab) % NSTG) * STG;                                          \
-    _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                            \
-      const uint32_t m0v_ = __builtin_amdgcn_readfirstlane(sb_ + (q * 4 + wave) * 16 * SROW);  \
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v_),           \
-                   "v"(src[q] + (long)(slab) * SK)                                             \
-                   : "memory", "m0");                                                          \
-    }                                                                                          \
+    const uint32_t m0v_ = __builtin_amdgcn_readfirstlane(                                      \
+        lds0 + ((slot) % NSTG) * STG + ((q) * 4 + wave) * 16 * SROW);                          \
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v_),             \
+                 "v"(src[q] + (long)(from) * SK)                                               \
+                 : "memory", "m0");                                                            \
   }
+  // operand fragment g of K-step ks of a slab: g < 4 reads A rows, else B rows
+#define POETX_FRAG(F, slab, ks, g)                                                             \
+  {                                                                                            \
+    const char* S_ = smem + ((slab) % NSTG) * STG;                                             \
+    const int c_ = (ks) * 2 + lane / 32;                                                       \
+    if ((g) < 4)                                                                               \
+      fa[F][(g) & 3] = as_bf16x8(*reinterpret_cast<const uint4*>(                              \
+          S_ + off32(wm * TM + ((g) & 3) * 32 + lane % 32, c_)));                              \
+    else                                                                                       \
+      fb[F][(g) & 3] = as_bf16x8(*reinterpret_cast<const uint4*>(                              \
+          S_ + BM * SROW + off32(wn * TN + ((g) & 3) * 32 + lane % 32, c_)));                  \
+  }
+  // MFMAs 2g, 2g+1 of a K-step (row fragment g/2, column fragments 2(g%2)+{0,1})
+#define POETX_MMA2(F, g)                                                                       \
+  acc[(g) / 2][2 * ((g) % 2)] =                                                                \
+      mfma32x32x16(fa[F][(g) / 2], fb[F][2 * ((g) % 2)], acc[(g) / 2][2 * ((g) % 2)]);        \
+  acc[(g) / 2][2 * ((g) % 2) + 1] =                                                            \
+      mfma32x32x16(fa[F][(g) / 2], fb[F][2 * ((g) % 2) + 1], acc[(g) / 2][2 * ((g) % 2) + 1]);
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16_t){};
   bf16x8_t fa[2][FM], fb[2][FN];
-#define POETX_FLOAD(F, slab, ks)                                                               \
-  {                                                                                            \
-    const char* S_ = smem + ((slab) % NSTG) * STG;                                             \
-    const int c_ = (ks) * 2 + lane / 32;                                                       \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[F][i] = as_bf16x8(                       \
-        *reinterpret_cast<const uint4*>(S_ + off32(wm * TM + i * 32 + lane % 32, c_)));        \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[F][j] = as_bf16x8(                       \
-        *reinterpret_cast<const uint4*>(S_ + BM * SROW + off32(wn * TN + j * 32 + lane % 32, c_))); \
-  }
-#define POETX_MMA(F)                                                                           \
-  _Pragma("unroll") for (int i = 0; i < FM; ++i) _Pragma("unroll") for (int j = 0; j < FN; ++j) \
-      acc[i][j] = mfma32x32x16(fa[F][i], fb[F][j], acc[i][j]);                                 \
-  _Pragma("unroll") for (int q = 0; q < 8; ++q) {                                              \
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* one LDS read */                      \
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* one MFMA */                          \
-  }                                                                                            \
-  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   const int nk = K / SK;
-  POETX_DMA(0);
-  if (nk > 1) POETX_DMA(1);
-  if (nk > 2) POETX_DMA(2);
-  if (nk > 3) POETX_DMA(3);
-  // vmcnt counts this wave's DMA instructions, 8 per slab, completing in order
-  if (nk > 3) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if (nk > 2) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if (nk > 1) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // Every stage is always filled: slab numbers past the end are clamped to
+  // the last slab, whose copy then lands in a stage that is never read.  So
+  // each wave always has exactly 8 DMA instructions per slab in flight and
+  // the vmcnt thresholds are constants.
+#pragma unroll
+  for (int p = 0; p < NSTG; ++p)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) POETX_DMA1(p, min(p, nk - 1), q);
+  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // slab 0 has landed (this wave's part)
   __syncthreads();
-  POETX_FLOAD(0, 0, 0);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) POETX_FRAG(0, 0, 0, g);
   for (int kt = 0; kt < nk; ++kt) {
-    POETX_FLOAD(1, kt, 1);
-    POETX_MMA(0);
-    // slab kt+1 has landed once at most the two slabs after it are pending;
-    // lgkmcnt(0): this wave's reads of slab kt are complete
-    const int ahead = min(2, nk - 2 - kt);
-    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
-    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    // K-step 0 of slab kt; the fragments of K-step 1 are read in between
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      POETX_FRAG(1, kt, 1, g);
+      POETX_MMA2(0, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // slab kt+1 has landed when at most the two slabs after it are pending;
+    // lgkmcnt(0): this wave's reads of slab kt are complete, so after the
+    // barrier slab kt's stage can be refilled
+    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    if (kt + NSTG < nk) POETX_DMA(kt + NSTG);  // into slab kt's stage, now free
-    if (kt + 1 < nk) POETX_FLOAD(0, kt + 1, 0);
-    POETX_MMA(1);
+    // K-step 1 of slab kt, with the first fragments of slab kt+1 and the
+    // DMA of slab kt+NSTG (into slab kt's stage) in between
+    const int refill = min(kt + NSTG, nk - 1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      POETX_FRAG(0, kt + 1, 0, g);
+      POETX_MMA2(1, g);
+      POETX_DMA1(kt, refill, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
-#undef POETX_DMA
-#undef POETX_FLOAD
-#undef POETX_MMA
+#undef POETX_DMA1
+#undef POETX_FRAG
+#undef POETX_MMA2
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
