@@ -125,8 +125,7 @@ def main() -> int:
                           L.dx, L.dG_P, L.dG_R, L.ws_bwd)
         lib().poetx_set_stage_events(None, 0)
         cnp_ev[s][2].record(stream)
-        P.poetx_cnp_bwd(L.theta_R, L.dG_R, L.b, L.k, L.dtheta_R, L.act, ws=L.ws_cnp_bwd)
-        P.poetx_cnp_bwd(L.theta_P, L.dG_P, L.b, L.k, L.dtheta_P, L.act, ws=L.ws_cnp_bwd)
+        L.cnp_bwd()
         cnp_ev[s][3].record(stream)
     torch.cuda.synchronize()
 

@@ -39,20 +39,62 @@ enum { MODE_FWD = 0, MODE_BWD1 = 1, MODE_BWD2 = 2 };
 
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); }
 
-// Qg[blk] = Q as bf16, one thread per packed parameter (coalesced reads),
-// plus the zero diagonal
-__global__ void k_unpack_q(int b, const float* __restrict__ theta, bf16* __restrict__ Qg) {
-  const int blk = blockIdx.y;
+// Triangle tiles: a b x b block splits into 64 x 64 tiles (I, J), I <= J;
+// tile pair p of a block enumerates them row by row.
+constexpr int TT = 64;
+__device__ __forceinline__ void tile_pair(int p, int nt, int& I, int& J) {
+  I = 0;
+  while (p >= nt - I) {
+    p -= nt - I;
+    ++I;
+  }
+  J = I + p;
+}
+
+// Qg[blk] = Q as bf16.  One workgroup per tile pair (I, J): the packed
+// parameters of tile (I, J) (row segments, contiguous in theta) go to LDS;
+// tile (I, J) of Q is written from it and tile (J, I) = -(tile)^T from the
+// transposed LDS reads, both with 16-byte row stores.  Diagonal tiles hold
+// both halves and the zero diagonal.
+__global__ __launch_bounds__(256) void k_unpack_q(int b, const float* __restrict__ theta,
+                                                  bf16* __restrict__ Qg) {
+  __shared__ float tile[TT][TT + 1];
+  const int blk = blockIdx.y, nt = b / TT;
   const int tb = b * (b - 1) / 2;
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  int I, J;
+  tile_pair(blockIdx.x, nt, I, J);
+  const float* th = theta + (long)blk * tb;
   bf16* q = Qg + (long)blk * b * b;
-  if (t < b) q[(long)t * b + t] = 0;
-  if (t >= tb) return;
-  int i, j;
-  tri_rc(t, b, i, j);
-  const float v = theta[(long)blk * tb + t];
-  q[(long)i * b + j] = f2bf(v);
-  q[(long)j * b + i] = f2bf(-v);
+  for (int e = threadIdx.x; e < TT * TT; e += 256) {
+    const int r = e / TT, c = e % TT, i = I * TT + r, j = J * TT + c;
+    tile[r][c] = i < j ? th[tri_index(i, j, b)] : 0.0f;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < TT * TT / 8; e += 256) {
+    const int r = e / (TT / 8), c0 = (e % (TT / 8)) * 8;
+    const int i = I * TT + r;
+    float up[8], lo[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = J * TT + c0 + u;
+      // row i of tile (I, J); on a diagonal tile the lower half is -theta(j, i)
+      up[u] = i < j ? tile[r][c0 + u] : (i == j ? 0.0f : -tile[c0 + u][r]);
+      lo[u] = -tile[c0 + u][r];  // row J*TT + r of tile (J, I)
+    }
+    uint4 v;
+    v.x = pack2bf(up[0], up[1]);
+    v.y = pack2bf(up[2], up[3]);
+    v.z = pack2bf(up[4], up[5]);
+    v.w = pack2bf(up[6], up[7]);
+    *reinterpret_cast<uint4*>(q + (long)i * b + J * TT + c0) = v;
+    if (I != J) {
+      v.x = pack2bf(lo[0], lo[1]);
+      v.y = pack2bf(lo[2], lo[3]);
+      v.z = pack2bf(lo[4], lo[5]);
+      v.w = pack2bf(lo[6], lo[7]);
+      *reinterpret_cast<uint4*>(q + (long)(J * TT + r) * b + I * TT + c0) = v;
+    }
+  }
 }
 
 // Copy the unpacked block Qg [B][B] into the padded LDS tile (row pitch
@@ -250,14 +292,31 @@ __global__ __launch_bounds__(NT, 1) void k_cnp_panel(int k, const float* __restr
 }
 
 // dtheta[t(i,j)] (+)= gQ[i][j] - gQ[j][i], one workgroup per (row i, block)
-__global__ void k_pack_skew(int b, const float* __restrict__ dQ, float* __restrict__ dtheta,
-                            int accumulate) {
-  const int i = blockIdx.x, blk = blockIdx.y;
+// dtheta(i, j) = dQ[i][j] - dQ[j][i] for i < j (set or accumulate).  One
+// workgroup per tile pair (I, J): tiles (I, J) and (J, I) of dQ are read with
+// row-contiguous loads into LDS; the packed outputs of tile (I, J) are row
+// segments of dtheta.
+__global__ __launch_bounds__(256) void k_pack_skew(int b, const float* __restrict__ dQ,
+                                                   float* __restrict__ dtheta, int accumulate) {
+  __shared__ float up[TT][TT + 1], lo[TT][TT + 1];
+  const int blk = blockIdx.y, nt = b / TT;
+  int I, J;
+  tile_pair(blockIdx.x, nt, I, J);
   const float* g = dQ + (long)blk * b * b;
-  float* dth = dtheta + (long)blk * (b * (b - 1) / 2) + tri_index(i, i + 1, b) - (i + 1);
-  for (int j = i + 1 + threadIdx.x; j < b; j += blockDim.x) {
-    float v = g[(long)i * b + j] - g[(long)j * b + i];
-    dth[j] = accumulate ? dth[j] + v : v;
+  float* dth = dtheta + (long)blk * (b * (b - 1) / 2);
+  for (int e = threadIdx.x; e < TT * TT; e += 256) {
+    const int r = e / TT, c = e % TT;
+    up[r][c] = g[(long)(I * TT + r) * b + J * TT + c];
+    lo[r][c] = g[(long)(J * TT + r) * b + I * TT + c];
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < TT * TT; e += 256) {
+    const int r = e / TT, c = e % TT, i = I * TT + r, j = J * TT + c;
+    if (i < j) {
+      const float v = up[r][c] - lo[c][r];
+      float* d = dth + tri_index(i, j, b);
+      *d = accumulate ? *d + v : v;
+    }
   }
 }
 
@@ -295,9 +354,8 @@ hipError_t dispatch_panel(int nblk, int b, int k, const float* theta, const bf16
 // every block size reads Q from this bf16 copy: blocks up to 256 stage it in
 // LDS, larger ones stream it through L2 as the MFMA A operand
 hipError_t unpack(int nblk, int b, const float* theta, bf16* Qg, hipStream_t s) {
-  const int tb = b * (b - 1) / 2;
-  hipLaunchKernelGGL(k_unpack_q, dim3((unsigned)((tb + 255) / 256), nblk), dim3(256), 0, s, b,
-                     theta, Qg);
+  const int nt = b / TT;
+  hipLaunchKernelGGL(k_unpack_q, dim3(nt * (nt + 1) / 2, nblk), dim3(256), 0, s, b, theta, Qg);
   return hipGetLastError();
 }
 
@@ -321,8 +379,9 @@ hipError_t launch_cnp_panel_bwd(int nblk, int b, int k, const float* theta, cons
   }
   e = dispatch_panel<MODE_BWD2>(nblk, b, k, theta, ws_Q, dG, ws_F, nullptr, ws_dQ, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_pack_skew, dim3(b - 1, nblk), dim3(256), 0, s, b, ws_dQ, dtheta,
-                     accumulate);
+  const int nt = b / TT;
+  hipLaunchKernelGGL(k_pack_skew, dim3(nt * (nt + 1) / 2, nblk), dim3(256), 0, s, b, ws_dQ,
+                     dtheta, accumulate);
   return hipGetLastError();
 }
 

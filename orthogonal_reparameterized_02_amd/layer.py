@@ -36,22 +36,27 @@ class POETXLayer:
         self.perm_R = e(m, d=torch.int32)
         self.perm_P_inv = e(n, d=torch.int32)
         self.perm_R_inv = e(m, d=torch.int32)
-        self.G_P, self.GT_P = e(nP, b, b), e(nP, b, b)
-        self.G_R, self.GT_R = e(nR, b, b), e(nR, b, b)
+        # Both sides share one block array (P blocks first, then R), so one
+        # Cayley-Neumann call covers the nP + nR blocks of a step; the
+        # per-side tensors are views.
+        nb = nP + nR
+        tb = b * (b - 1) // 2
+        self.G, self.GT = e(nb, b, b), e(nb, b, b)
+        self.G_P, self.G_R = self.G[:nP], self.G[nP:]
+        self.GT_P, self.GT_R = self.GT[:nP], self.GT[nP:]
         self.y = e(T, m)
         self.dx = e(T, n)
-        self.dG_P = e(nP, b, b, d=torch.float32)
-        self.dG_R = e(nR, b, b, d=torch.float32)
-        tb = b * (b - 1) // 2
-        self.dtheta_P = e(nP, tb, d=torch.float32)
-        self.dtheta_R = e(nR, tb, d=torch.float32)
+        self.dG = e(nb, b, b, d=torch.float32)
+        self.dG_P, self.dG_R = self.dG[:nP], self.dG[nP:]
+        self.theta = torch.zeros(nb, tb, dtype=torch.float32, device=dev)
+        self.theta_P, self.theta_R = self.theta[:nP], self.theta[nP:]
+        self.dtheta = e(nb, tb, d=torch.float32)
+        self.dtheta_P, self.dtheta_R = self.dtheta[:nP], self.dtheta[nP:]
         self.saved = _bytes(P.poetx_saved_bytes(self.sh), dev)
         self.ws_fwd = _bytes(P.poetx_workspace_bytes(self.sh, 0), dev)
         self.ws_bwd = _bytes(P.poetx_workspace_bytes(self.sh, 1), dev)
-        nmax = max(nP, nR)
-        self.ws_cnp_fwd = _bytes(P.poetx_cnp_workspace_bytes(nmax, b, k, 0, act), dev)
-        self.ws_cnp_bwd = _bytes(P.poetx_cnp_workspace_bytes(nmax, b, k, 1, act), dev)
-        self.theta_P = self.theta_R = None
+        self.ws_cnp_fwd = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 0, act), dev)
+        self.ws_cnp_bwd = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 1, act), dev)
 
     # -- set-up, once per inner loop (untimed) --------------------------------
     def load(self, W0: torch.Tensor, theta_P: torch.Tensor, theta_R: torch.Tensor,
@@ -61,13 +66,21 @@ class POETXLayer:
         W0 = W0.to(self.device, self.dtype).contiguous()
         P.poetx_fold_perm(W0, self.perm_R, self.perm_P, self.W0f, self.W0fT,
                           self.perm_R_inv, self.perm_P_inv)
-        self.theta_P = theta_P.to(self.device, torch.float32).contiguous()
-        self.theta_R = theta_R.to(self.device, torch.float32).contiguous()
+        self.set_theta(theta_P, theta_R)
+
+    def set_theta(self, theta_P: torch.Tensor, theta_R: torch.Tensor) -> None:
+        self.theta_P.copy_(theta_P)
+        self.theta_R.copy_(theta_R)
 
     # -- the hot path ---------------------------------------------------------
     def cnp(self) -> None:
-        P.poetx_cnp_fwd(self.theta_P, self.b, self.k, self.G_P, self.GT_P, self.ws_cnp_fwd)
-        P.poetx_cnp_fwd(self.theta_R, self.b, self.k, self.G_R, self.GT_R, self.ws_cnp_fwd)
+        """G, G^T of every block of both sides, in one call."""
+        P.poetx_cnp_fwd(self.theta, self.b, self.k, self.G, self.GT, self.ws_cnp_fwd)
+
+    def cnp_bwd(self) -> None:
+        """dtheta of both sides from dG, in one call."""
+        P.poetx_cnp_bwd(self.theta, self.dG, self.b, self.k, self.dtheta, self.act,
+                        ws=self.ws_cnp_bwd)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         self.cnp()
@@ -78,10 +91,7 @@ class POETXLayer:
     def backward(self, dy: torch.Tensor):
         P.poetx_layer_bwd(self.sh, dy, self.GT_P, self.GT_R, self.W0fT, self.perm_P_inv,
                           self.perm_R, self.saved, self.dx, self.dG_P, self.dG_R, self.ws_bwd)
-        P.poetx_cnp_bwd(self.theta_R, self.dG_R, self.b, self.k, self.dtheta_R, self.act,
-                        ws=self.ws_cnp_bwd)
-        P.poetx_cnp_bwd(self.theta_P, self.dG_P, self.b, self.k, self.dtheta_P, self.act,
-                        ws=self.ws_cnp_bwd)
+        self.cnp_bwd()
         return self.dx, self.dtheta_P, self.dtheta_R
 
     def step(self, x: torch.Tensor, dy: torch.Tensor):
@@ -93,8 +103,7 @@ class POETXLayer:
 class _POETXFn(torch.autograd.Function):
     @staticmethod
     def forward(ctx, x, theta_P, theta_R, layer: POETXLayer):
-        layer.theta_P = theta_P.detach().contiguous()
-        layer.theta_R = theta_R.detach().contiguous()
+        layer.set_theta(theta_P.detach(), theta_R.detach())
         y = layer.forward(x.contiguous()).clone()
         ctx.layer = layer
         return y
