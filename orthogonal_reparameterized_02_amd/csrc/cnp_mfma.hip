@@ -65,9 +65,18 @@ __global__ __launch_bounds__(256) void k_unpack_q(int b, const float* __restrict
   tile_pair(blockIdx.x, nt, I, J);
   const float* th = theta + (long)blk * tb;
   bf16* q = Qg + (long)blk * b * b;
-  for (int e = threadIdx.x; e < TT * TT; e += 256) {
-    const int r = e / TT, c = e % TT, i = I * TT + r, j = J * TT + c;
-    tile[r][c] = i < j ? th[tri_index(i, j, b)] : 0.0f;
+  constexpr int PER = TT * TT / 256;
+  float v[PER];  // every load in flight before the first LDS write
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = u * 256 + threadIdx.x;
+    const int i = I * TT + e / TT, j = J * TT + e % TT;
+    v[u] = i < j ? th[tri_index(i, j, b)] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = u * 256 + threadIdx.x;
+    tile[e / TT][e % TT] = v[u];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < TT * TT / 8; e += 256) {
@@ -304,10 +313,19 @@ __global__ __launch_bounds__(256) void k_pack_skew(int b, const float* __restric
   tile_pair(blockIdx.x, nt, I, J);
   const float* g = dQ + (long)blk * b * b;
   float* dth = dtheta + (long)blk * (b * (b - 1) / 2);
-  for (int e = threadIdx.x; e < TT * TT; e += 256) {
-    const int r = e / TT, c = e % TT;
-    up[r][c] = g[(long)(I * TT + r) * b + J * TT + c];
-    lo[r][c] = g[(long)(J * TT + r) * b + I * TT + c];
+  constexpr int PER = TT * TT / 256;
+  float vu[PER], vl[PER];  // every load in flight before the first LDS write
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = u * 256 + threadIdx.x, r = e / TT, c = e % TT;
+    vu[u] = g[(long)(I * TT + r) * b + J * TT + c];
+    vl[u] = g[(long)(J * TT + r) * b + I * TT + c];
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = u * 256 + threadIdx.x;
+    up[e / TT][e % TT] = vu[u];
+    lo[e / TT][e % TT] = vl[u];
   }
   __syncthreads();
   for (int e = threadIdx.x; e < TT * TT; e += 256) {
