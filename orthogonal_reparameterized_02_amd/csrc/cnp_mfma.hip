@@ -128,7 +128,7 @@ __device__ __forceinline__ void q_to_lds(const bf16* __restrict__ Qb, bf16* Qs, 
 }
 
 template <int B, bool QLDS, int MODE>
-__global__ __launch_bounds__(NT, 1) void k_cnp_panel(int k, const float* __restrict__ theta,
+__global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_cnp_panel(int k, const float* __restrict__ theta,
                                                   const bf16* __restrict__ Qg,
                                                   const float* __restrict__ D,
                                                   bf16* __restrict__ out_bf, bf16* __restrict__ out_bfT,
@@ -149,26 +149,92 @@ __global__ __launch_bounds__(NT, 1) void k_cnp_panel(int k, const float* __restr
   const float* Db = D ? D + boff : nullptr;
   const float* th = theta + (long)blk * (B * (B - 1) / 2);
 
-  if constexpr (QLDS) q_to_lds<B, NT>(Qb, Qs, QP);
+  // Prologue: every global load (Q, and for phase 1 the band D[J0..J0+31][:])
+  // goes out before the first LDS write.
+  constexpr int QPER = B * (B / 8) / NT;  // 16-byte Q vectors per thread
+  // (native vector types: the HIP vector structs are copied through memcpy,
+  // which keeps conditionally stored arrays out of registers)
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
+  u32x4_t qv[QLDS ? QPER : 1];
+  if constexpr (QLDS) {
+#pragma unroll
+    for (int u = 0; u < QPER; ++u) {
+      const int q = u * NT + threadIdx.x;
+      qv[u] = *reinterpret_cast<const u32x4_t*>(Qb + (q / (B / 8)) * B + (q % (B / 8)) * 8);
+    }
+  }
+  constexpr int DPER = MODE == MODE_BWD1 ? PW * B / 4 / NT : 1;  // float4 of the D band
+  f32x4_t dv[DPER];
+  if constexpr (MODE == MODE_BWD1) {
+#pragma unroll
+    for (int u = 0; u < DPER; ++u)
+      dv[u] = *reinterpret_cast<const f32x4_t*>(Db + (long)J0 * B + 4 * (u * NT + threadIdx.x));
+  }
 
-  // fixed part of the per-step addend, in accumulator layout
+  // fixed part of the per-step addend, in accumulator layout:
+  //   forward  Q[row][J0+c]   (from the bf16 Q in LDS when it is there: the
+  //                            products use that same rounded Q)
+  //   phase 1  D^T[row][c] = D[J0+c][row]  (the D band, transposed through LDS)
+  //   phase 2  D[row][J0+c]                (row-contiguous global loads)
   float base[RTW][16];
+#pragma unroll
+  for (int t = 0; t < RTW; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) base[t][r] = 0.f;
+  if constexpr (MODE == MODE_BWD1) {
+    // two passes of 16 band rows through the Xs region as fp32 [16][B + 4]
+    float* band = reinterpret_cast<float*>(Xs);
+    constexpr int BP = B + 4;
+    static_assert(16 * BP * 4 <= PW * QP * 2, "band pass fits in Xs");
+#define POETX_BAND_PASS(pass)                                                                  \
+  {                                                                                            \
+    _Pragma("unroll") for (int u = 0; u < DPER; ++u) {                                         \
+      const int e = 4 * (u * NT + threadIdx.x);                                                \
+      if (e / B / 16 == (pass))                                                                \
+        *reinterpret_cast<f32x4_t*>(band + (e / B - 16 * (pass)) * BP + e % B) = dv[u];        \
+    }                                                                                          \
+    __syncthreads();                                                                           \
+    if (col / 16 == (pass)) {                                                                  \
+      _Pragma("unroll") for (int t = 0; t < RTW; ++t) {                                        \
+        const int rt = wave + t * NWAVE;                                                       \
+        if (rt < RT) {                                                                         \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) base[t][r] =                          \
+              band[(col - 16 * (pass)) * BP + rt * 32 + acc_row(r, lane)];                     \
+        }                                                                                      \
+      }                                                                                        \
+    }                                                                                          \
+    __syncthreads();                                                                           \
+  }
+    POETX_BAND_PASS(0);
+    POETX_BAND_PASS(1);
+#undef POETX_BAND_PASS
+  }
+  if constexpr (QLDS) {
+#pragma unroll
+    for (int u = 0; u < QPER; ++u) {
+      const int q = u * NT + threadIdx.x;
+      *reinterpret_cast<u32x4_t*>(Qs + (q / (B / 8)) * QP + (q % (B / 8)) * 8) = qv[u];
+    }
+    if constexpr (MODE == MODE_FWD) __syncthreads();  // Q visible for the base
+  }
   f32x16_t X[RTW];
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
     const int rt = wave + t * NWAVE;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float bv = 0.f;
       if (rt < RT) {
         const int row = rt * 32 + acc_row(r, lane);
-        if (MODE == MODE_FWD) bv = skew_at_nb(th, row, J0 + col, B);     // Q[row][J0+c]
-        else if (MODE == MODE_BWD1) bv = Db[(long)(J0 + col) * B + row];  // D^T[row][c]
-        else bv = Db[(long)row * B + J0 + col];                          // D[row][J0+c]
+        if constexpr (MODE == MODE_FWD) {
+          if constexpr (QLDS) base[t][r] = bf2f(Qs[row * QP + J0 + col]);
+          else base[t][r] = skew_at_nb(th, row, J0 + col, B);
+        } else if constexpr (MODE == MODE_BWD2) {
+          base[t][r] = Db[(long)row * B + J0 + col];
+        }
       }
-      base[t][r] = bv;
       // initial state: U_k = Q (forward), w_{k+1} D^T or w_{k+1} D (backward)
-      X[t][r] = (MODE == MODE_FWD) ? bv : cnp_wcoef(k + 1, k) * bv;
+      X[t][r] = (MODE == MODE_FWD) ? base[t][r] : cnp_wcoef(k + 1, k) * base[t][r];
     }
   }
 
