@@ -59,6 +59,74 @@ __global__ __launch_bounds__(PERM_THREADS) void k_permute_rows_lds(
   }
 }
 
+// The main form: RPW rows per workgroup of NTHR threads, each thread owning
+// up to MAXV 16-byte output vectors per row.  Every row load and the
+// thread's indices (16-byte vector loads) go out before the first LDS write;
+// one barrier, then each thread gathers its vectors of every row from LDS.
+template <typename E, int NTHR, int RPW, int MAXV>
+__global__ __launch_bounds__(NTHR) void k_permute_rows_v(int rows, int width,
+                                                         const E* __restrict__ in,
+                                                         const int32_t* __restrict__ rmap,
+                                                         const int32_t* __restrict__ idx,
+                                                         E* __restrict__ out) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  typedef __attribute__((ext_vector_type(4))) int32_t i32x4;
+  constexpr int PER = 16 / sizeof(E);  // elements per vector
+  constexpr int IV = PER / 4;          // index vectors per output vector
+  const int nv = width / PER;
+  const int r0 = blockIdx.x * RPW;
+  u32x4 ld[RPW][MAXV];
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    const long src = r0 + rr < rows ? (rmap ? (long)rmap[r0 + rr] : (long)(r0 + rr)) : 0;
+    const u32x4* s4 = reinterpret_cast<const u32x4*>(in + src * width);
+#pragma unroll
+    for (int u = 0; u < MAXV; ++u) {
+      const int v = u * NTHR + threadIdx.x;
+      if (v < nv && r0 + rr < rows) ld[rr][u] = __builtin_nontemporal_load(s4 + v);
+    }
+  }
+  i32x4 ix[MAXV][IV];
+#pragma unroll
+  for (int u = 0; u < MAXV; ++u) {
+    const int v = u * NTHR + threadIdx.x;
+#pragma unroll
+    for (int h = 0; h < IV; ++h)
+      if (v < nv) ix[u][h] = reinterpret_cast<const i32x4*>(idx)[v * IV + h];
+  }
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+    for (int u = 0; u < MAXV; ++u) {
+      const int v = u * NTHR + threadIdx.x;
+      if (v < nv && r0 + rr < rows) reinterpret_cast<u32x4*>(smem + (size_t)rr * width * sizeof(E))[v] = ld[rr][u];
+    }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < RPW; ++rr) {
+    if (r0 + rr >= rows) break;
+    const E* row = reinterpret_cast<const E*>(smem + (size_t)rr * width * sizeof(E));
+#pragma unroll
+    for (int u = 0; u < MAXV; ++u) {
+      const int v = u * NTHR + threadIdx.x;
+      if (v < nv) {
+        E t[PER];
+#pragma unroll
+        for (int h = 0; h < IV; ++h) {
+          t[4 * h + 0] = row[ix[u][h].x];
+          t[4 * h + 1] = row[ix[u][h].y];
+          t[4 * h + 2] = row[ix[u][h].z];
+          t[4 * h + 3] = row[ix[u][h].w];
+        }
+        uint4 pk;
+        __builtin_memcpy(&pk, t, 16);
+        reinterpret_cast<uint4*>(out + (long)(r0 + rr) * width)[v] = pk;
+      }
+    }
+  }
+}
+
 // rows too wide for LDS: gather straight from global memory
 template <typename E>
 __global__ __launch_bounds__(PERM_THREADS) void k_permute_rows_direct(
@@ -94,11 +162,29 @@ __global__ void k_inverse_perm(int n, const int32_t* __restrict__ p, int32_t* __
   if (i < n) inv[p[i]] = i;
 }
 
+template <typename E, int MAXV>
+hipError_t permute_v_launch(int rows, int width, const void* in, const int32_t* rmap,
+                            const int32_t* idx, void* out, hipStream_t s) {
+  constexpr int NTHR = 512, RPW = 2;
+  const int grid = (rows + RPW - 1) / RPW;
+  hipLaunchKernelGGL((k_permute_rows_v<E, NTHR, RPW, MAXV>), dim3(grid), dim3(NTHR),
+                     RPW * width * sizeof(E), s, rows, width, (const E*)in, rmap, idx, (E*)out);
+  return hipGetLastError();
+}
+
 template <typename E>
 hipError_t permute_impl(int rows, int width, const void* in, const int32_t* rmap,
                         const int32_t* idx, void* out, hipStream_t s) {
   const size_t bytes = (size_t)width * sizeof(E);
   const int grid = rows < 65536 ? rows : 65536;
+  const bool aligned = bytes % 16 == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0 &&
+                       (uintptr_t)idx % 16 == 0;
+  if (aligned && 2 * bytes <= PERM_LDS_MAX && rows < (1 << 30)) {
+    const int nv = (int)(bytes / 16);
+    if (nv <= 512) return permute_v_launch<E, 1>(rows, width, in, rmap, idx, out, s);
+    if (nv <= 1024) return permute_v_launch<E, 2>(rows, width, in, rmap, idx, out, s);
+    return permute_v_launch<E, 4>(rows, width, in, rmap, idx, out, s);
+  }
   if (bytes <= PERM_LDS_MAX) {
     int vec = (bytes % 16 == 0) && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
     hipLaunchKernelGGL(k_permute_rows_lds<E>, dim3(grid), dim3(PERM_THREADS), bytes, s, rows,
