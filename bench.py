@@ -42,7 +42,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="square")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB elementwise copy "
@@ -196,7 +196,7 @@ def main() -> int:
 
 
 COPY_PROBE_BYTES = 1 << 30
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_gemm_nt_block_square_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_nt4_block_square_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "orthogonal_reparameterized_02_amd", "csrc", "gemm_mfma.hip")
 
 
