@@ -44,6 +44,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--xmem", action="store_true",
+                    help="memory-saving mode: keep only U, recompute Z in the backward")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB elementwise copy "
                          "(torch.neg) three times: the reference kernel that calibrates "
@@ -73,7 +75,7 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act)
+    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act, xmem=args.xmem)
     L.load(dev(d["W0"]), dev(d["theta_P"]), dev(d["theta_R"]), dev(d["perm_P"]), dev(d["perm_R"]))
     x, dy = dev(d["x"]), dev(d["dy"])
     torch.cuda.synchronize()
@@ -118,11 +120,9 @@ def main() -> int:
         L.cnp()
         cnp_ev[s][1].record(stream)
         hook(fwd_ev[s])
-        P.poetx_layer_fwd(L.sh, x, L.G_P, L.G_R, L.W0f, L.perm_P, L.perm_R_inv, L.y, L.saved,
-                          L.ws_fwd)
+        L.layer_fwd(x)
         hook(bwd_ev[s])
-        P.poetx_layer_bwd(L.sh, dy, L.GT_P, L.GT_R, L.W0fT, L.perm_P_inv, L.perm_R, L.saved,
-                          L.dx, L.dG_P, L.dG_R, L.ws_bwd)
+        L.layer_bwd(dy)
         lib().poetx_set_stage_events(None, 0)
         cnp_ev[s][2].record(stream)
         L.cnp_bwd()
@@ -173,7 +173,8 @@ def main() -> int:
         "dtype": "bf16" if act == P.BF16 else "f32",
         "data": "synthetic (seeded Gaussian activations and weights, random permutations)",
         "config": {"workload": f"{cfg.name}: POET-X layer m={m} n={n} b={b} k={cfg.k} "
-                               f"T={T} tokens, {cfg.dtype} activations/W0, fp32 theta",
+                               f"T={T} tokens, {cfg.dtype} activations/W0, fp32 theta"
+                               + (", xmem (Z recomputed in the backward)" if args.xmem else ""),
                    "m": m, "n": n, "b": b, "k": cfg.k, "tokens": T, "seed": args.seed},
         "mfma_peak_frac": flops / (ms * 1e-3) / (peak * 1e12),
         "step_tflops": flops / (ms * 1e-3) / 1e12,

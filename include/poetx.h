@@ -183,6 +183,36 @@ int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P,
                         void* ws, size_t ws_bytes, poetx_stream_t stream);
 
 /*
+ * poetx_layer_fwd_xmem / poetx_layer_bwd_xmem -- the memory-saving mode
+ * ("POET-X ...", technical summary 2.5: recompute in the backward pass
+ * instead of keeping intermediates).  The forward keeps only U = x[:, pi_P]
+ * in `saved` (poetx_saved_bytes_xmem(sh) bytes) and writes Z to its
+ * workspace; the backward first recomputes V = U G_P^T and Z = V W0f^T with
+ * the forward's own kernels, then runs as poetx_layer_bwd.  Outputs are
+ * bitwise equal to those of poetx_layer_fwd / poetx_layer_bwd; the saved
+ * buffer is T*m*sizeof(act) bytes smaller and the backward does one more
+ * dense product (2 T m n flops) and one more block product (2 T n b flops).
+ *   fwd: arguments as poetx_layer_fwd; ws poetx_workspace_bytes(sh, 2) bytes.
+ *   bwd: arguments as poetx_layer_bwd plus
+ *        G_P [n/b][b][b] (act) and W0f [m][n] (act);
+ *        ws poetx_workspace_bytes(sh, 3) bytes.
+ * Errors: ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE.
+ */
+int32_t poetx_layer_fwd_xmem(const poetx_shape* sh, const void* x, const void* G_P,
+                             const void* G_R, const void* W0f, const int32_t* perm_P,
+                             const int32_t* perm_R_inv, void* y, void* saved,
+                             void* ws, size_t ws_bytes, poetx_stream_t stream);
+int32_t poetx_layer_bwd_xmem(const poetx_shape* sh, const void* dy, const void* G_P,
+                             const void* GT_P, const void* GT_R, const void* W0f,
+                             const void* W0fT, const int32_t* perm_P_inv,
+                             const int32_t* perm_R, const void* saved, void* dx,
+                             float* dG_P, float* dG_R, void* ws, size_t ws_bytes,
+                             poetx_stream_t stream);
+
+/* Bytes of the saved-activation buffer of the xmem mode; 0 on bad arguments. */
+size_t poetx_saved_bytes_xmem(const poetx_shape* sh);
+
+/*
  * poetx_set_stage_events -- timing hook for profilers and benchmarks.
  * While set, each poetx_layer_fwd / poetx_layer_bwd call on the calling
  * thread records events[i] (hipEvent_t handles owned by the caller) on its
@@ -197,8 +227,8 @@ int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P,
  */
 int32_t poetx_set_stage_events(void* const* events, int32_t count);
 
-/* Scratch bytes for poetx_layer_fwd (which = 0) or poetx_layer_bwd (1);
- * 0 on bad arguments. */
+/* Scratch bytes for poetx_layer_fwd (which = 0), poetx_layer_bwd (1),
+ * poetx_layer_fwd_xmem (2) or poetx_layer_bwd_xmem (3); 0 on bad arguments. */
 size_t poetx_workspace_bytes(const poetx_shape* sh, int32_t which);
 
 /* Bytes of the saved-activation buffer; 0 on bad arguments. */

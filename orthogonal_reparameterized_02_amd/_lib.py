@@ -28,6 +28,10 @@ SIGNATURES = {
     "poetx_layer_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "poetx_workspace_bytes": (_sz, [_p, _i]),
     "poetx_saved_bytes": (_sz, [_p]),
+    "poetx_layer_fwd_xmem": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "poetx_layer_bwd_xmem": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
+                                  _p]),
+    "poetx_saved_bytes_xmem": (_sz, [_p]),
     "poetx_set_stage_events": (_i, [_p, _i]),
 }
 

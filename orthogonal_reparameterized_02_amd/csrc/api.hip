@@ -104,19 +104,22 @@ inline void mark(int i, hipStream_t s) {
 inline bool use_mfma(const poetx_shape* sh) { return sh->act == POETX_BF16 && sh->b >= 64; }
 
 // workspace layout of the layer calls
-struct FwdWs { size_t V, S, total; };
-struct BwdWs { size_t dS, dZ, dV, dU, part, total; };
+// (xmem: the forward's Z, or the backward's recomputed Z, lives in the
+// workspace instead of the saved buffer)
+struct FwdWs { size_t V, S, Z, total; };
+struct BwdWs { size_t dS, dZ, dV, dU, part, Z, total; };
 
-FwdWs fwd_ws(const poetx_shape* sh) {
+FwdWs fwd_ws(const poetx_shape* sh, bool xmem = false) {
   const size_t es = es_of(sh->act), T = sh->T;
   FwdWs w;
   w.V = 0;
   w.S = w.V + align_up(T * sh->n * es);
-  w.total = w.S + align_up(T * sh->m * es);
+  w.Z = w.S + align_up(T * sh->m * es);
+  w.total = w.Z + (xmem ? align_up(T * sh->m * es) : 0);
   return w;
 }
 
-BwdWs bwd_ws(const poetx_shape* sh) {
+BwdWs bwd_ws(const poetx_shape* sh, bool xmem = false) {
   const size_t es = es_of(sh->act), T = sh->T;
   BwdWs w;
   w.dS = 0;
@@ -130,15 +133,16 @@ BwdWs bwd_ws(const poetx_shape* sh) {
     const size_t pp = tn_partial_bytes(sh->n / sh->b, sh->b, sh->T);
     part = align_up(pr > pp ? pr : pp);
   }
-  w.total = w.part + part;
+  w.Z = w.part + part;
+  w.total = w.Z + (xmem ? align_up((size_t)sh->T * sh->m * es) : 0);
   return w;
 }
 
 // saved activations: U = x[:, pi_P] then Z
 size_t saved_U(const poetx_shape*) { return 0; }
 size_t saved_Z(const poetx_shape* sh) { return align_up((size_t)sh->T * sh->n * es_of(sh->act)); }
-size_t saved_total(const poetx_shape* sh) {
-  return saved_Z(sh) + align_up((size_t)sh->T * sh->m * es_of(sh->act));
+size_t saved_total(const poetx_shape* sh, bool xmem = false) {
+  return xmem ? saved_Z(sh) : saved_Z(sh) + align_up((size_t)sh->T * sh->m * es_of(sh->act));
 }
 
 template <typename TS> TS* at(void* base, size_t off) {
@@ -184,13 +188,13 @@ hipError_t tn(bool mfma, int batch, int D, int T, const TS* A, long lda, const T
 template <typename TS>
 int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const TS* G_R,
                        const TS* W0f, const int32_t* perm_P, const int32_t* perm_R_inv, TS* y,
-                       void* saved, void* ws, hipStream_t s) {
+                       void* saved, void* ws, hipStream_t s, bool xmem) {
   const int m = sh->m, n = sh->n, b = sh->b, T = sh->T;
   const int es = (int)sizeof(TS);
   const bool mf = use_mfma(sh);
-  const FwdWs w = fwd_ws(sh);
+  const FwdWs w = fwd_ws(sh, xmem);
   TS* U = at<TS>(saved, saved_U(sh));
-  TS* Z = at<TS>(saved, saved_Z(sh));
+  TS* Z = xmem ? at<TS>(ws, w.Z) : at<TS>(saved, saved_Z(sh));
   TS* V = at<TS>(ws, w.V);
   TS* S = at<TS>(ws, w.S);
   const long bb = (long)b * b;
@@ -233,13 +237,13 @@ template <typename TS>
 int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, const TS* GT_R,
                        const TS* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
                        const void* saved, TS* dx, float* dG_P, float* dG_R, void* ws,
-                       hipStream_t s) {
+                       hipStream_t s, const TS* G_P = nullptr, const TS* W0f = nullptr) {
   const int m = sh->m, n = sh->n, b = sh->b, T = sh->T;
   const int es = (int)sizeof(TS);
   const bool mf = use_mfma(sh);
-  const BwdWs w = bwd_ws(sh);
+  const bool xmem = G_P != nullptr;
+  const BwdWs w = bwd_ws(sh, xmem);
   const TS* U = at<TS>(saved, saved_U(sh));
-  const TS* Z = at<TS>(saved, saved_Z(sh));
   TS* dS = at<TS>(ws, w.dS);
   TS* dZ = at<TS>(ws, w.dZ);
   TS* dV = at<TS>(ws, w.dV);
@@ -247,6 +251,29 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   float* part = at<float>(ws, w.part);
   const long bb = (long)b * b;
   hipError_t e;
+  const TS* Z;
+  if (xmem) {
+    // recompute V = U G_P^T (into dU's space, free until the end) and
+    // Z = V W0f^T with the kernels the forward used, so Z is bitwise the same
+    TS* V = dU;
+    TS* Zr = at<TS>(ws, w.Z);
+    if ((e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
+      return dev_fail(e, "recompute V");
+    bool done = false;
+    if constexpr (sizeof(TS) == 2) {
+      if (mf && mfma_nt_block_ok(T, m, n, b)) {
+        if ((e = launch_mfma_nt_block(T, m, n, V, n, W0f, n, Zr, m, nullptr, nullptr, 0, s)) !=
+            hipSuccess)
+          return dev_fail(e, "recompute Z");
+        done = true;
+      }
+    }
+    if (!done && (e = nt<TS>(mf, 1, T, m, n, V, n, 0, W0f, n, 0, Zr, m, 0, s)) != hipSuccess)
+      return dev_fail(e, "recompute Z");
+    Z = Zr;
+  } else {
+    Z = at<TS>(saved, saved_Z(sh));
+  }
   mark(0, s);
   // dS = dy[:, pi_R]
   if ((e = launch_permute_cols(T, m, es, dy, perm_R, dS, s)) != hipSuccess) return dev_fail(e, "gather dy");
@@ -395,6 +422,8 @@ size_t poetx_workspace_bytes(const poetx_shape* sh, int32_t which) {
   if (check_shape("poetx_workspace_bytes", sh) != POETX_OK) return 0;
   if (which == 0) return fwd_ws(sh).total;
   if (which == 1) return bwd_ws(sh).total;
+  if (which == 2) return fwd_ws(sh, true).total;
+  if (which == 3) return bwd_ws(sh, true).total;
   return 0;
 }
 
@@ -403,10 +432,15 @@ size_t poetx_saved_bytes(const poetx_shape* sh) {
   return saved_total(sh);
 }
 
-int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P, const void* G_R,
-                        const void* W0f, const int32_t* perm_P, const int32_t* perm_R_inv,
-                        void* y, void* saved, void* ws, size_t ws_bytes, poetx_stream_t stream) {
-  const char* fn = "poetx_layer_fwd";
+size_t poetx_saved_bytes_xmem(const poetx_shape* sh) {
+  if (check_shape("poetx_saved_bytes_xmem", sh) != POETX_OK) return 0;
+  return saved_total(sh, true);
+}
+
+static int32_t layer_fwd_entry(const char* fn, bool xmem, const poetx_shape* sh, const void* x,
+                               const void* G_P, const void* G_R, const void* W0f,
+                               const int32_t* perm_P, const int32_t* perm_R_inv, void* y,
+                               void* saved, void* ws, size_t ws_bytes, poetx_stream_t stream) {
   int32_t st = check_shape(fn, sh);
   if (st != POETX_OK) return st;
   NEED_PTR(x);
@@ -418,24 +452,44 @@ int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P, c
   NEED_PTR(y);
   NEED_PTR(saved);
   NEED_PTR(ws);
-  const size_t need = fwd_ws(sh).total;
+  const size_t need = fwd_ws(sh, xmem).total;
   if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   if (sh->act == POETX_BF16)
     return layer_fwd_impl<bf16>(sh, (const bf16*)x, (const bf16*)G_P, (const bf16*)G_R,
-                                (const bf16*)W0f, perm_P, perm_R_inv, (bf16*)y, saved, ws, s);
+                                (const bf16*)W0f, perm_P, perm_R_inv, (bf16*)y, saved, ws, s, xmem);
   return layer_fwd_impl<float>(sh, (const float*)x, (const float*)G_P, (const float*)G_R,
-                               (const float*)W0f, perm_P, perm_R_inv, (float*)y, saved, ws, s);
+                               (const float*)W0f, perm_P, perm_R_inv, (float*)y, saved, ws, s,
+                               xmem);
 }
 
-int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P, const void* GT_R,
-                        const void* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
-                        const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
-                        size_t ws_bytes, poetx_stream_t stream) {
-  const char* fn = "poetx_layer_bwd";
+int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P, const void* G_R,
+                        const void* W0f, const int32_t* perm_P, const int32_t* perm_R_inv,
+                        void* y, void* saved, void* ws, size_t ws_bytes, poetx_stream_t stream) {
+  return layer_fwd_entry("poetx_layer_fwd", false, sh, x, G_P, G_R, W0f, perm_P, perm_R_inv, y,
+                         saved, ws, ws_bytes, stream);
+}
+
+int32_t poetx_layer_fwd_xmem(const poetx_shape* sh, const void* x, const void* G_P,
+                             const void* G_R, const void* W0f, const int32_t* perm_P,
+                             const int32_t* perm_R_inv, void* y, void* saved, void* ws,
+                             size_t ws_bytes, poetx_stream_t stream) {
+  return layer_fwd_entry("poetx_layer_fwd_xmem", true, sh, x, G_P, G_R, W0f, perm_P, perm_R_inv,
+                         y, saved, ws, ws_bytes, stream);
+}
+
+static int32_t layer_bwd_entry(const char* fn, bool xmem, const poetx_shape* sh, const void* dy,
+                               const void* G_P, const void* GT_P, const void* GT_R,
+                               const void* W0f, const void* W0fT, const int32_t* perm_P_inv,
+                               const int32_t* perm_R, const void* saved, void* dx, float* dG_P,
+                               float* dG_R, void* ws, size_t ws_bytes, poetx_stream_t stream) {
   int32_t st = check_shape(fn, sh);
   if (st != POETX_OK) return st;
   NEED_PTR(dy);
+  if (xmem) {
+    NEED_PTR(G_P);
+    NEED_PTR(W0f);
+  }
   NEED_PTR(GT_P);
   NEED_PTR(GT_R);
   NEED_PTR(W0fT);
@@ -446,16 +500,35 @@ int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P,
   NEED_PTR(dG_P);
   NEED_PTR(dG_R);
   NEED_PTR(ws);
-  const size_t need = bwd_ws(sh).total;
+  const size_t need = bwd_ws(sh, xmem).total;
   if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
   if (sh->act == POETX_BF16)
     return layer_bwd_impl<bf16>(sh, (const bf16*)dy, (const bf16*)GT_P, (const bf16*)GT_R,
                                 (const bf16*)W0fT, perm_P_inv, perm_R, saved, (bf16*)dx, dG_P,
-                                dG_R, ws, s);
+                                dG_R, ws, s, xmem ? (const bf16*)G_P : nullptr,
+                                (const bf16*)W0f);
   return layer_bwd_impl<float>(sh, (const float*)dy, (const float*)GT_P, (const float*)GT_R,
                                (const float*)W0fT, perm_P_inv, perm_R, saved, (float*)dx, dG_P,
-                               dG_R, ws, s);
+                               dG_R, ws, s, xmem ? (const float*)G_P : nullptr,
+                               (const float*)W0f);
+}
+
+int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P, const void* GT_R,
+                        const void* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
+                        const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
+                        size_t ws_bytes, poetx_stream_t stream) {
+  return layer_bwd_entry("poetx_layer_bwd", false, sh, dy, nullptr, GT_P, GT_R, nullptr, W0fT,
+                         perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws, ws_bytes, stream);
+}
+
+int32_t poetx_layer_bwd_xmem(const poetx_shape* sh, const void* dy, const void* G_P,
+                             const void* GT_P, const void* GT_R, const void* W0f,
+                             const void* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
+                             const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
+                             size_t ws_bytes, poetx_stream_t stream) {
+  return layer_bwd_entry("poetx_layer_bwd_xmem", true, sh, dy, G_P, GT_P, GT_R, W0f, W0fT,
+                         perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -54,7 +54,8 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
                           hipStream_t s);
 // C = A B^T as above (one batch) and, per 256-column tile g of C (one
-// orthogonal block of size 256), E[:, g] = C[:, g] Bk[g]^T with Bk [N/256][256][256]
+// orthogonal block of size 256), E[:, g] = C[:, g] Bk[g]^T with Bk [N/256][256][256].
+// E == nullptr: C only, from the same main loop (bitwise the same C).
 bool mfma_nt_block_ok(int M, int N, int K, int b);
 hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
                                 long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,

@@ -23,8 +23,12 @@ def _bytes(n: int, device) -> torch.Tensor:
 class POETXLayer:
     """Buffers and calls for one (m, n, b, k, T, dtype) layer."""
 
-    def __init__(self, m: int, n: int, b: int, k: int, T: int, act: int, device="cuda"):
+    def __init__(self, m: int, n: int, b: int, k: int, T: int, act: int, device="cuda",
+                 xmem: bool = False):
+        """xmem: keep only U for the backward pass and recompute Z there
+        (the memory-saving mode) instead of keeping U and Z."""
         self.m, self.n, self.b, self.k, self.T, self.act = m, n, b, k, T, act
+        self.xmem = xmem
         self.sh = P.shape(m, n, b, k, T, act)
         dt = self.dtype = _DT[act]
         dev = self.device = torch.device(device)
@@ -52,9 +56,14 @@ class POETXLayer:
         self.theta_P, self.theta_R = self.theta[:nP], self.theta[nP:]
         self.dtheta = e(nb, tb, d=torch.float32)
         self.dtheta_P, self.dtheta_R = self.dtheta[:nP], self.dtheta[nP:]
-        self.saved = _bytes(P.poetx_saved_bytes(self.sh), dev)
-        self.ws_fwd = _bytes(P.poetx_workspace_bytes(self.sh, 0), dev)
-        self.ws_bwd = _bytes(P.poetx_workspace_bytes(self.sh, 1), dev)
+        if xmem:
+            self.saved = _bytes(P.poetx_saved_bytes_xmem(self.sh), dev)
+            self.ws_fwd = _bytes(P.poetx_workspace_bytes(self.sh, 2), dev)
+            self.ws_bwd = _bytes(P.poetx_workspace_bytes(self.sh, 3), dev)
+        else:
+            self.saved = _bytes(P.poetx_saved_bytes(self.sh), dev)
+            self.ws_fwd = _bytes(P.poetx_workspace_bytes(self.sh, 0), dev)
+            self.ws_bwd = _bytes(P.poetx_workspace_bytes(self.sh, 1), dev)
         self.ws_cnp_fwd = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 0, act), dev)
         self.ws_cnp_bwd = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 1, act), dev)
 
@@ -84,13 +93,28 @@ class POETXLayer:
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         self.cnp()
-        P.poetx_layer_fwd(self.sh, x, self.G_P, self.G_R, self.W0f, self.perm_P,
-                          self.perm_R_inv, self.y, self.saved, self.ws_fwd)
+        self.layer_fwd(x)
         return self.y
 
+    def layer_fwd(self, x: torch.Tensor) -> None:
+        """The layer forward alone (G_P, G_R already formed)."""
+        fwd = P.poetx_layer_fwd_xmem if self.xmem else P.poetx_layer_fwd
+        fwd(self.sh, x, self.G_P, self.G_R, self.W0f, self.perm_P, self.perm_R_inv, self.y,
+            self.saved, self.ws_fwd)
+
+    def layer_bwd(self, dy: torch.Tensor) -> None:
+        """The layer backward alone (dx, dG_P, dG_R)."""
+        if self.xmem:
+            P.poetx_layer_bwd_xmem(self.sh, dy, self.G_P, self.GT_P, self.GT_R, self.W0f,
+                                   self.W0fT, self.perm_P_inv, self.perm_R, self.saved, self.dx,
+                                   self.dG_P, self.dG_R, self.ws_bwd)
+        else:
+            P.poetx_layer_bwd(self.sh, dy, self.GT_P, self.GT_R, self.W0fT, self.perm_P_inv,
+                              self.perm_R, self.saved, self.dx, self.dG_P, self.dG_R,
+                              self.ws_bwd)
+
     def backward(self, dy: torch.Tensor):
-        P.poetx_layer_bwd(self.sh, dy, self.GT_P, self.GT_R, self.W0fT, self.perm_P_inv,
-                          self.perm_R, self.saved, self.dx, self.dG_P, self.dG_R, self.ws_bwd)
+        self.layer_bwd(dy)
         self.cnp_bwd()
         return self.dx, self.dtheta_P, self.dtheta_R
 

@@ -72,6 +72,10 @@ def poetx_saved_bytes(sh: Shape) -> int:
     return lib().poetx_saved_bytes(C.byref(sh))
 
 
+def poetx_saved_bytes_xmem(sh: Shape) -> int:
+    return lib().poetx_saved_bytes_xmem(C.byref(sh))
+
+
 def poetx_cnp_fwd(theta: torch.Tensor, b: int, k: int, G: torch.Tensor,
                   GT: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                   stream=None) -> None:
@@ -138,6 +142,38 @@ def poetx_layer_bwd(sh: Shape, dy, GT_P, GT_R, W0fT, perm_P_inv, perm_R, saved, 
     check("poetx_layer_bwd", lib().poetx_layer_bwd(
         C.byref(sh), _dev(dy, "dy", dt, T * m), _dev(GT_P, "GT_P", dt, n * b),
         _dev(GT_R, "GT_R", dt, m * b), _dev(W0fT, "W0fT", dt, m * n),
+        _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(perm_R, "perm_R", torch.int32, m),
+        _dev(saved, "saved"), _dev(dx, "dx", dt, T * n), _dev(dG_P, "dG_P", torch.float32, n * b),
+        _dev(dG_R, "dG_R", torch.float32, m * b), wp, wb, _stream(stream)))
+
+
+def poetx_layer_fwd_xmem(sh: Shape, x, G_P, G_R, W0f, perm_P, perm_R_inv, y, saved, ws,
+                         stream=None) -> None:
+    dt = _DT[sh.act]
+    m, n, b, T = sh.m, sh.n, sh.b, sh.T
+    need_ws, need_saved = poetx_workspace_bytes(sh, 2), poetx_saved_bytes_xmem(sh)
+    wp, wb = _ws(ws, need_ws)
+    if saved.numel() * saved.element_size() < need_saved:
+        raise ValueError(f"saved: {need_saved} bytes required")
+    check("poetx_layer_fwd_xmem", lib().poetx_layer_fwd_xmem(
+        C.byref(sh), _dev(x, "x", dt, T * n), _dev(G_P, "G_P", dt, n * b),
+        _dev(G_R, "G_R", dt, m * b), _dev(W0f, "W0f", dt, m * n),
+        _dev(perm_P, "perm_P", torch.int32, n), _dev(perm_R_inv, "perm_R_inv", torch.int32, m),
+        _dev(y, "y", dt, T * m), _dev(saved, "saved"), wp, wb, _stream(stream)))
+
+
+def poetx_layer_bwd_xmem(sh: Shape, dy, G_P, GT_P, GT_R, W0f, W0fT, perm_P_inv, perm_R, saved,
+                         dx, dG_P, dG_R, ws, stream=None) -> None:
+    dt = _DT[sh.act]
+    m, n, b, T = sh.m, sh.n, sh.b, sh.T
+    need_ws, need_saved = poetx_workspace_bytes(sh, 3), poetx_saved_bytes_xmem(sh)
+    wp, wb = _ws(ws, need_ws)
+    if saved.numel() * saved.element_size() < need_saved:
+        raise ValueError(f"saved: {need_saved} bytes required")
+    check("poetx_layer_bwd_xmem", lib().poetx_layer_bwd_xmem(
+        C.byref(sh), _dev(dy, "dy", dt, T * m), _dev(G_P, "G_P", dt, n * b),
+        _dev(GT_P, "GT_P", dt, n * b), _dev(GT_R, "GT_R", dt, m * b),
+        _dev(W0f, "W0f", dt, m * n), _dev(W0fT, "W0fT", dt, m * n),
         _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(perm_R, "perm_R", torch.int32, m),
         _dev(saved, "saved"), _dev(dx, "dx", dt, T * n), _dev(dG_P, "dG_P", torch.float32, n * b),
         _dev(dG_R, "dG_R", torch.float32, m * b), wp, wb, _stream(stream)))

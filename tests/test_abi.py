@@ -106,6 +106,30 @@ def test_layer_argument_errors():
     assert L.poetx_fold_perm(4, 4, 1, FAKE, None, FAKE, FAKE, None, None, None, None) == 1
 
 
+def test_xmem_argument_errors_and_sizes():
+    L = _lib.lib()
+    good = _lib.Shape(4096, 4096, 256, 4, 8192, 1)
+    fast, mem = L.poetx_saved_bytes(C.byref(good)), L.poetx_saved_bytes_xmem(C.byref(good))
+    assert mem > 0 and fast - mem >= 8192 * 4096 * 2   # Z is not kept
+    for which in (2, 3):
+        assert L.poetx_workspace_bytes(C.byref(good), which) > \
+            L.poetx_workspace_bytes(C.byref(good), which - 2)
+    assert L.poetx_workspace_bytes(C.byref(good), 4) == 0
+    need = L.poetx_workspace_bytes(C.byref(good), 2)
+    assert L.poetx_layer_fwd_xmem(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, need - 1, None) == 3
+    need = L.poetx_workspace_bytes(C.byref(good), 3)
+    # the recompute needs G_P and W0f
+    assert L.poetx_layer_bwd_xmem(C.byref(good), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+    assert b"G_P" in L.poetx_last_error()
+    assert L.poetx_layer_bwd_xmem(C.byref(good), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+    assert b"W0f" in L.poetx_last_error()
+    assert L.poetx_layer_bwd_xmem(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 3
+
+
 def test_binding_rejects_host_tensors():
     import torch
     from orthogonal_reparameterized_02_amd import poetx as P

@@ -223,6 +223,51 @@ def test_repeat_runs_bitwise_equal():
         np.testing.assert_array_equal(a, bits(t))
 
 
+# ------------------------------------------------------------------ xmem mode
+@pytest.mark.parametrize("name,T", [("probe", 64), ("mid", 200), ("square", 96),
+                                    ("mlp13b", 40), ("square", 8192)])
+def test_xmem_bitwise_equals_xfast(name, T):
+    """The memory-saving mode keeps only U and recomputes Z in the backward
+    with the forward's own kernels, so every output equals the default
+    mode's bit for bit; its saved buffer is T*m elements smaller."""
+    cfg = I.CONFIG_BY_NAME[name]
+    say(f"xmem {name} T={T}")
+    d = I.make_inputs(cfg, seed=21, T=T)
+    outs = []
+    for xmem in (False, True):
+        L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype), xmem=xmem)
+        L.load(to_dev(d["W0"]), to_dev(d["theta_P"]), to_dev(d["theta_R"]),
+               to_dev(d["perm_P"]), to_dev(d["perm_R"]))
+        L.step(to_dev(d["x"]), to_dev(d["dy"]))
+        torch.cuda.synchronize()
+        outs.append([bits(t).copy() for t in (L.y, L.dx, L.dG_P, L.dG_R, L.dtheta_P, L.dtheta_R)])
+        if xmem:
+            es = 2 if cfg.dtype == "bf16" else 4
+            assert (P.poetx_saved_bytes(L.sh) - P.poetx_saved_bytes_xmem(L.sh)) >= T * cfg.m * es
+        del L
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_xmem_parity_small_T():
+    """The memory-saving mode against the oracle directly."""
+    cfg = I.CONFIG_BY_NAME["square"]
+    T = 72
+    d = I.make_inputs(cfg, seed=23, T=T)
+    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype), xmem=True)
+    L.load(to_dev(d["W0"]), to_dev(d["theta_P"]), to_dev(d["theta_R"]),
+           to_dev(d["perm_P"]), to_dev(d["perm_R"]))
+    L.step(to_dev(d["x"]), to_dev(d["dy"]))
+    torch.cuda.synchronize()
+    y_ref, _ = O.layer_fwd(d["x64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
+                           d["perm_R"], cfg.b, cfg.k)
+    g = O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
+                    d["perm_R"], cfg.b, cfg.k)
+    for got, ref in ((L.y, y_ref), (L.dx, g["dx"]), (L.dtheta_P, g["dtheta_P"]),
+                     (L.dtheta_R, g["dtheta_R"])):
+        assert O.rel_fro(to_f64(got), ref) <= TOL[cfg.dtype]
+
+
 def test_autograd_module_matches_layer():
     from orthogonal_reparameterized_02_amd.layer import POETXLinear
     torch.manual_seed(0)
