@@ -139,6 +139,19 @@ def main() -> int:
     stages["cnp_fwd"] = mean_ms(cnp_ev, 0, 1) * 1e3
     stages["cnp_bwd"] = mean_ms(cnp_ev, 2, 3) * 1e3
 
+    # ---- once per inner loop (not part of the step): merge W0 <- R W0 P ----
+    merge_ws = torch.empty(P.poetx_workspace_bytes(L.sh, 4), dtype=torch.uint8, device="cuda")
+    merged = torch.empty(cfg.m, cfg.n, dtype=L.dtype, device="cuda")
+    mev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for i in range(6):
+        if i == 1:
+            mev[0].record(stream)
+        P.poetx_merge(L.sh, L.W0f, L.G_R, L.GT_P, L.perm_R_inv, L.perm_P_inv, merged, merge_ws)
+    mev[1].record(stream)
+    torch.cuda.synchronize()
+    merge_us = mev[0].elapsed_time(mev[1]) / 5 * 1e3
+    del merge_ws, merged
+
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
@@ -181,6 +194,7 @@ def main() -> int:
         "cnp_blocks_per_s": {"fwd": nblocks / (stages["cnp_fwd"] * 1e-6),
                              "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
+        "inner_loop_merge_us": round(merge_us, 2),
         "roofline": {"kernel": ("k_nt4<1>: Z = V W0f^T with S = Z G_R^T "
                                 "in the epilogue" if fused else "k_gemm_nt: Z = V W0f^T"),
                      "bound": "mfma", "achieved": dense_tflops, "peak": peak,

@@ -213,6 +213,28 @@ int32_t poetx_layer_bwd_xmem(const poetx_shape* sh, const void* dy, const void* 
 size_t poetx_saved_bytes_xmem(const poetx_shape* sh);
 
 /*
+ * poetx_merge -- end of an inner loop ("POET-X ...", technical summary 2.1:
+ * the learned transforms are merged into the weight, W <- R W P, before new
+ * ones start from the identity; 2.2: new permutations are then drawn and
+ * folded).  Writes the current effective weight
+ *   W0_out = R W0 P = Pi_R^T BD(G_R) W0f BD(G_P) Pi_P,
+ *   W0_out[a][c] = M[pi_R^{-1}[a]][pi_P^{-1}[c]],  M = BD(G_R) W0f BD(G_P),
+ * with two block products (4 m n b flops), two transposes and the
+ * permutation.  The caller then resets theta to 0, draws new permutations
+ * and calls poetx_fold_perm on W0_out.  T in `sh` is not used.
+ *   W0f   [m][n]        folded weight (act)
+ *   G_R   [m/b][b][b]   R-side blocks (act), GT_P [n/b][b][b] P-side blocks
+ *                       transposed (act), both from poetx_cnp_fwd
+ *   perm_R_inv [m], perm_P_inv [n]  from poetx_fold_perm
+ *   W0_out [m][n] (act); must not alias W0f
+ *   ws    poetx_workspace_bytes(sh, 4) bytes of scratch.
+ * Errors: ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE.
+ */
+int32_t poetx_merge(const poetx_shape* sh, const void* W0f, const void* G_R,
+                    const void* GT_P, const int32_t* perm_R_inv, const int32_t* perm_P_inv,
+                    void* W0_out, void* ws, size_t ws_bytes, poetx_stream_t stream);
+
+/*
  * poetx_set_stage_events -- timing hook for profilers and benchmarks.
  * While set, each poetx_layer_fwd / poetx_layer_bwd call on the calling
  * thread records events[i] (hipEvent_t handles owned by the caller) on its
@@ -228,7 +250,8 @@ size_t poetx_saved_bytes_xmem(const poetx_shape* sh);
 int32_t poetx_set_stage_events(void* const* events, int32_t count);
 
 /* Scratch bytes for poetx_layer_fwd (which = 0), poetx_layer_bwd (1),
- * poetx_layer_fwd_xmem (2) or poetx_layer_bwd_xmem (3); 0 on bad arguments. */
+ * poetx_layer_fwd_xmem (2), poetx_layer_bwd_xmem (3) or poetx_merge (4);
+ * 0 on bad arguments. */
 size_t poetx_workspace_bytes(const poetx_shape* sh, int32_t which);
 
 /* Bytes of the saved-activation buffer; 0 on bad arguments. */

@@ -32,6 +32,7 @@ SIGNATURES = {
     "poetx_layer_bwd_xmem": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
                                   _p]),
     "poetx_saved_bytes_xmem": (_sz, [_p]),
+    "poetx_merge": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "poetx_set_stage_events": (_i, [_p, _i]),
 }
 

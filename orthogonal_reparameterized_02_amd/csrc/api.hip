@@ -138,6 +138,11 @@ BwdWs bwd_ws(const poetx_shape* sh, bool xmem = false) {
   return w;
 }
 
+// merge: two [m][n] scratch matrices
+size_t merge_ws(const poetx_shape* sh) {
+  return 2 * align_up((size_t)sh->m * sh->n * es_of(sh->act));
+}
+
 // saved activations: U = x[:, pi_P] then Z
 size_t saved_U(const poetx_shape*) { return 0; }
 size_t saved_Z(const poetx_shape* sh) { return align_up((size_t)sh->T * sh->n * es_of(sh->act)); }
@@ -319,6 +324,31 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   return ok();
 }
 
+// W0_out = Pi_R^T BD(G_R) W0f BD(G_P) Pi_P
+template <typename TS>
+int32_t merge_impl(const poetx_shape* sh, const TS* W0f, const TS* G_R, const TS* GT_P,
+                   const int32_t* perm_R_inv, const int32_t* perm_P_inv, TS* W0_out, void* ws,
+                   hipStream_t s) {
+  const int m = sh->m, n = sh->n, b = sh->b;
+  const int es = (int)sizeof(TS);
+  const bool mf = use_mfma(sh);
+  TS* A = at<TS>(ws, 0);
+  TS* Bm = at<TS>(ws, align_up((size_t)m * n * es));
+  hipError_t e;
+  // A = W0f BD(G_P): the rows of W0f are the "tokens" of a P-side block
+  // product with B operand G_P^T
+  if ((e = blocks<TS>(mf, n / b, m, n, b, W0f, GT_P, A, s)) != hipSuccess)
+    return dev_fail(e, "merge: W0f BD(G_P)");
+  if ((e = launch_transpose(m, n, es, A, Bm, s)) != hipSuccess) return dev_fail(e, "merge: transpose");
+  // A = (BD(G_R) W0f BD(G_P))^T = Bm BD(G_R)^T, [n][m]
+  if ((e = blocks<TS>(mf, m / b, n, m, b, Bm, G_R, A, s)) != hipSuccess)
+    return dev_fail(e, "merge: BD(G_R) rows");
+  if ((e = launch_transpose(n, m, es, A, Bm, s)) != hipSuccess) return dev_fail(e, "merge: transpose");
+  if ((e = launch_permute_rows_cols(m, n, es, Bm, perm_R_inv, perm_P_inv, W0_out, s)) != hipSuccess)
+    return dev_fail(e, "merge: unfold");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -424,6 +454,7 @@ size_t poetx_workspace_bytes(const poetx_shape* sh, int32_t which) {
   if (which == 1) return bwd_ws(sh).total;
   if (which == 2) return fwd_ws(sh, true).total;
   if (which == 3) return bwd_ws(sh, true).total;
+  if (which == 4) return merge_ws(sh);
   return 0;
 }
 
@@ -529,6 +560,30 @@ int32_t poetx_layer_bwd_xmem(const poetx_shape* sh, const void* dy, const void* 
                              size_t ws_bytes, poetx_stream_t stream) {
   return layer_bwd_entry("poetx_layer_bwd_xmem", true, sh, dy, G_P, GT_P, GT_R, W0f, W0fT,
                          perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws, ws_bytes, stream);
+}
+
+int32_t poetx_merge(const poetx_shape* sh, const void* W0f, const void* G_R, const void* GT_P,
+                    const int32_t* perm_R_inv, const int32_t* perm_P_inv, void* W0_out, void* ws,
+                    size_t ws_bytes, poetx_stream_t stream) {
+  const char* fn = "poetx_merge";
+  int32_t st = check_shape(fn, sh);
+  if (st != POETX_OK) return st;
+  NEED_PTR(W0f);
+  NEED_PTR(G_R);
+  NEED_PTR(GT_P);
+  NEED_PTR(perm_R_inv);
+  NEED_PTR(perm_P_inv);
+  NEED_PTR(W0_out);
+  NEED_PTR(ws);
+  if (W0_out == W0f) return fail(POETX_ERR_ARG, "%s: W0_out must not alias W0f", fn);
+  const size_t need = merge_ws(sh);
+  if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  if (sh->act == POETX_BF16)
+    return merge_impl<bf16>(sh, (const bf16*)W0f, (const bf16*)G_R, (const bf16*)GT_P, perm_R_inv,
+                            perm_P_inv, (bf16*)W0_out, ws, s);
+  return merge_impl<float>(sh, (const float*)W0f, (const float*)G_R, (const float*)GT_P,
+                           perm_R_inv, perm_P_inv, (float*)W0_out, ws, s);
 }
 
 }  // extern "C"

@@ -26,6 +26,12 @@ hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
 // out[r][c] = in[r][idx[c]] for r < rows, c < width; es = element bytes (2|4)
 hipError_t launch_permute_cols(int rows, int width, int es, const void* in,
                                const int32_t* idx, void* out, hipStream_t s);
+// out[r][c] = in[rmap[r]][idx[c]] ([rows][width], es = element bytes 2|4)
+hipError_t launch_permute_rows_cols(int rows, int width, int es, const void* in,
+                                    const int32_t* rmap, const int32_t* idx, void* out,
+                                    hipStream_t s);
+// out[j][i] = in[i][j], in [m][n]
+hipError_t launch_transpose(int m, int n, int es, const void* in, void* out, hipStream_t s);
 
 // ---- portable tiled kernels (simple.hip) ----------------------------------
 // C[bt][i][j] = sum_k A[bt][i][k] * B[bt][j][k]       (row-major, fp32 accumulate)

@@ -205,6 +205,26 @@ hipError_t launch_permute_cols(int rows, int width, int es, const void* in, cons
   return permute_impl<uint32_t>(rows, width, in, nullptr, idx, out, s);
 }
 
+hipError_t launch_permute_rows_cols(int rows, int width, int es, const void* in,
+                                    const int32_t* rmap, const int32_t* idx, void* out,
+                                    hipStream_t s) {
+  if (rows <= 0 || width <= 0) return hipSuccess;
+  if (es == 2) return permute_impl<uint16_t>(rows, width, in, rmap, idx, out, s);
+  return permute_impl<uint32_t>(rows, width, in, rmap, idx, out, s);
+}
+
+hipError_t launch_transpose(int m, int n, int es, const void* in, void* out, hipStream_t s) {
+  if (m <= 0 || n <= 0) return hipSuccess;
+  dim3 grid((n + 31) / 32, (m + 31) / 32);
+  if (es == 2)
+    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, m, n, (const uint16_t*)in,
+                       (uint16_t*)out);
+  else
+    hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(256), 0, s, m, n, (const uint32_t*)in,
+                       (uint32_t*)out);
+  return hipGetLastError();
+}
+
 hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
                        const int32_t* pP, void* W0f, void* W0fT, int32_t* pRinv,
                        int32_t* pPinv, hipStream_t s) {

@@ -77,6 +77,16 @@ class POETXLayer:
                           self.perm_R_inv, self.perm_P_inv)
         self.set_theta(theta_P, theta_R)
 
+    def merge(self, out: torch.Tensor = None) -> torch.Tensor:
+        """The weight R W0 P that the current theta and permutations
+        represent (G from the latest cnp()), as an [m, n] tensor."""
+        if out is None:
+            out = torch.empty(self.m, self.n, dtype=self.dtype, device=self.device)
+        ws = _bytes(P.poetx_workspace_bytes(self.sh, 4), self.device)
+        P.poetx_merge(self.sh, self.W0f, self.G_R, self.GT_P, self.perm_R_inv, self.perm_P_inv,
+                      out, ws)
+        return out
+
     def set_theta(self, theta_P: torch.Tensor, theta_R: torch.Tensor) -> None:
         self.theta_P.copy_(theta_P)
         self.theta_R.copy_(theta_R)
@@ -165,6 +175,19 @@ class POETXLinear(torch.nn.Module):
         pR = torch.randperm(self._layer.m, generator=self._gen).to(torch.int32)
         self._layer.load(self.W0, self.theta_P.detach(), self.theta_R.detach(),
                          pP.to(self.W0.device), pR.to(self.W0.device))
+
+    @torch.no_grad()
+    def end_inner_loop(self) -> None:
+        """Merge the learned transforms into the weight (W0 <- R W0 P), reset
+        theta to 0 (R = P = I) and start a new inner loop with new
+        permutations; the layer's function is unchanged by the merge."""
+        L = self._layer
+        L.set_theta(self.theta_P, self.theta_R)
+        L.cnp()
+        self.W0.copy_(L.merge())
+        self.theta_P.zero_()
+        self.theta_R.zero_()
+        self.start_inner_loop()
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         return _POETXFn.apply(x, self.theta_P, self.theta_R, self._layer)

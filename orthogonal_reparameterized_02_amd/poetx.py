@@ -177,3 +177,16 @@ def poetx_layer_bwd_xmem(sh: Shape, dy, G_P, GT_P, GT_R, W0f, W0fT, perm_P_inv, 
         _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(perm_R, "perm_R", torch.int32, m),
         _dev(saved, "saved"), _dev(dx, "dx", dt, T * n), _dev(dG_P, "dG_P", torch.float32, n * b),
         _dev(dG_R, "dG_R", torch.float32, m * b), wp, wb, _stream(stream)))
+
+
+def poetx_merge(sh: Shape, W0f, G_R, GT_P, perm_R_inv, perm_P_inv, W0_out, ws,
+                stream=None) -> None:
+    """W0_out = R W0 P, the weight the current transforms represent."""
+    dt = _DT[sh.act]
+    m, n, b = sh.m, sh.n, sh.b
+    wp, wb = _ws(ws, poetx_workspace_bytes(sh, 4))
+    check("poetx_merge", lib().poetx_merge(
+        C.byref(sh), _dev(W0f, "W0f", dt, m * n), _dev(G_R, "G_R", dt, m * b),
+        _dev(GT_P, "GT_P", dt, n * b), _dev(perm_R_inv, "perm_R_inv", torch.int32, m),
+        _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(W0_out, "W0_out", dt, m * n),
+        wp, wb, _stream(stream)))

@@ -114,7 +114,7 @@ def test_xmem_argument_errors_and_sizes():
     for which in (2, 3):
         assert L.poetx_workspace_bytes(C.byref(good), which) > \
             L.poetx_workspace_bytes(C.byref(good), which - 2)
-    assert L.poetx_workspace_bytes(C.byref(good), 4) == 0
+    assert L.poetx_workspace_bytes(C.byref(good), 5) == 0
     need = L.poetx_workspace_bytes(C.byref(good), 2)
     assert L.poetx_layer_fwd_xmem(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                   FAKE, need - 1, None) == 3
@@ -137,3 +137,20 @@ def test_binding_rejects_host_tensors():
     G = torch.zeros(2, 32, 32)
     with pytest.raises(ValueError, match="GPU tensor"):
         P.poetx_cnp_fwd(th, 32, 4, G)
+
+
+def test_merge_argument_errors():
+    L = _lib.lib()
+    good = _lib.Shape(4096, 4096, 256, 4, 8192, 1)
+    need = L.poetx_workspace_bytes(C.byref(good), 4)
+    assert need >= 2 * 4096 * 4096 * 2
+    OUT = C.c_void_p(0x20000)
+    assert L.poetx_merge(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, OUT, FAKE, need - 1,
+                         None) == 3
+    assert L.poetx_merge(C.byref(good), FAKE, None, FAKE, FAKE, FAKE, OUT, FAKE, need,
+                         None) == 1
+    assert b"G_R" in L.poetx_last_error()
+    # the output may not alias the folded weight
+    assert L.poetx_merge(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
+                         None) == 1
+    assert b"alias" in L.poetx_last_error()
