@@ -393,30 +393,52 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   constexpr int SLAB = BM * ROWB;
   acc_to_slabs<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane, 0, BM);
+  // EPI 1: E = C_tile Bk_g^T, K = 256.  The A operand is the C tile just
+  // staged in LDS (four 64-wide K slabs); the B fragments come straight from
+  // global memory (the block's G is 128 KB and read by every tile of its
+  // column, so it sits in L2), two K-steps ahead, so the loop has no barrier.
+  // The first loads go out before the C stores: vmcnt is in order, and a
+  // wait for loads issued after the stores would wait for the stores too.
+  const bf16* Gw = nullptr;
+  bf16x8_t gb[3][FN];
+  if constexpr (EPI == 1) {
+    Gw = Bk + (long)tn * 256 * 256 + (long)(wn * TN + lane % 32) * 256 + 8 * (lane / 32);
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        gb[f][j] = as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * 256 + f * 16));
+  }
   __syncthreads();
   slabs_to_global<BM, BN, NTH>(smem, Cm, ldc, m0, n0, M, N);
   if constexpr (EPI == 1) {
-    // as in k_gemm_nt: E = C_tile Bk_g^T from the staged tile, G slab by slab
-    using C = Cfg<BM, BN, 2, 2>;
-    const bf16* Bg = Bk + (long)tn * 256 * 256;
-    char* Gs = smem + 4 * SLAB;
-    constexpr int GP = 256 / C::RPP;
-    const int lr = tid / 8, lc = tid % 8;
-    uint4 gq[GP];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16_t){};
-    for (int ks = 0; ks < 4; ++ks) {
+    bf16x8_t ca[2][FM];
+#define POETX_CFRAG(F, ks)                                                                     \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) ca[F][i] = as_bf16x8(                       \
+        *reinterpret_cast<const uint4*>(smem + ((ks) / 4) * SLAB +                             \
+                                        lds_off(wm * TM + i * 32 + lane % 32,                  \
+                                                ((ks) % 4) * 2 + lane / 32)));
+    POETX_CFRAG(0, 0);
 #pragma unroll
-      for (int p = 0; p < GP; ++p)
-        gq[p] = *reinterpret_cast<const uint4*>(Bg + (long)(p * C::RPP + lr) * 256 + ks * BK + lc * 8);
+    for (int ks = 0; ks < 16; ++ks) {
+      if (ks + 2 < 16) {
 #pragma unroll
-      for (int p = 0; p < GP; ++p) *reinterpret_cast<uint4*>(Gs + lds_off(p * C::RPP + lr, lc)) = gq[p];
-      __syncthreads();  // G slab visible
-      mma_slab<C>(smem + ks * SLAB, Gs, acc, wm, wn, lane);
-      __syncthreads();  // every wave is done with this G slab (and, at the end, the C tile)
+        for (int j = 0; j < FN; ++j)
+          gb[(ks + 2) % 3][j] =
+              as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * 256 + (ks + 2) * 16));
+      }
+      if (ks + 1 < 16) { POETX_CFRAG((ks + 1) & 1, ks + 1); }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(ca[ks & 1][i], gb[ks % 3][j], acc[i][j]);
     }
+#undef POETX_CFRAG
+    __syncthreads();  // every wave is done with the C tile
     acc_to_slabs<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane, 0, BM);
     __syncthreads();
     slabs_to_global<BM, BN, NTH>(smem, E, lde, m0, n0, M, N);
