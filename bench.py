@@ -46,6 +46,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--xmem", action="store_true",
                     help="memory-saving mode: keep only U, recompute Z in the backward")
+    ap.add_argument("--xq", action="store_true",
+                    help="int8 base weight (per-row scales), expanded to bf16 in each pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after the timed steps, run a plain 1 GiB elementwise copy "
                          "(torch.neg) three times: the reference kernel that calibrates "
@@ -75,8 +77,14 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act, xmem=args.xmem)
-    L.load(dev(d["W0"]), dev(d["theta_P"]), dev(d["theta_R"]), dev(d["perm_P"]), dev(d["perm_R"]))
+    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act, xmem=args.xmem, xq=args.xq)
+    if args.xq:
+        q, sc = I.quantize_rows_int8(I.make_inputs(cfg, seed=args.seed, want=("W0",))["W064"])
+        L.load_q(torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda(), dev(d["theta_P"]),
+                 dev(d["theta_R"]), dev(d["perm_P"]), dev(d["perm_R"]))
+    else:
+        L.load(dev(d["W0"]), dev(d["theta_P"]), dev(d["theta_R"]), dev(d["perm_P"]),
+               dev(d["perm_R"]))
     x, dy = dev(d["x"]), dev(d["dy"])
     torch.cuda.synchronize()
 
@@ -187,7 +195,8 @@ def main() -> int:
         "data": "synthetic (seeded Gaussian activations and weights, random permutations)",
         "config": {"workload": f"{cfg.name}: POET-X layer m={m} n={n} b={b} k={cfg.k} "
                                f"T={T} tokens, {cfg.dtype} activations/W0, fp32 theta"
-                               + (", xmem (Z recomputed in the backward)" if args.xmem else ""),
+                               + (", xmem (Z recomputed in the backward)" if args.xmem else "")
+                               + (", xq (int8 base weight)" if args.xq else ""),
                    "m": m, "n": n, "b": b, "k": cfg.k, "tokens": T, "seed": args.seed},
         "mfma_peak_frac": flops / (ms * 1e-3) / (peak * 1e12),
         "step_tflops": flops / (ms * 1e-3) / 1e12,

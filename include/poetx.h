@@ -65,7 +65,8 @@ typedef enum {
   POETX_ERR_DEVICE = 4        /* HIP launch or device query failed          */
 } poetx_status;
 
-typedef enum { POETX_F32 = 0, POETX_BF16 = 1 } poetx_dtype;
+typedef enum { POETX_F32 = 0, POETX_BF16 = 1, POETX_I8 = 2 } poetx_dtype;
+/* POETX_I8 is a weight storage type only (poetx_fold_perm, poetx_dequant). */
 
 /* Shape of one layer.  m: outputs, n: inputs, b: block size (m % b == 0 and
  * n % b == 0), k: Neumann order (>= 0), T: tokens (>= 1), act: poetx_dtype.
@@ -141,6 +142,28 @@ int32_t poetx_fold_perm(int32_t m, int32_t n, int32_t dt, const void* W0,
                         const int32_t* perm_R, const int32_t* perm_P, void* W0f,
                         void* W0fT, int32_t* perm_R_inv, int32_t* perm_P_inv,
                         poetx_stream_t stream);
+
+/*
+ * POET-XQ ("POET-X ...", technical summary 2.6: training on a low-bit base
+ * model, INT8, dequantized on the fly when needed; the high-precision weight
+ * is never kept).  The base weight is held as int8 q with one fp32 scale per
+ * output row: W0[i][j] = s[i] * q[i][j].  poetx_fold_perm folds q
+ * (dt = POETX_I8) into q_f and q_fT; poetx_fold_scale folds the scales;
+ * poetx_dequant expands the folded weight to bf16 for one layer call.  The
+ * bf16 copy lives only in the caller's per-call scratch, so the persistent
+ * weight is the int8 one.
+ *
+ * poetx_fold_scale -- s_f[i] = s[perm_R[i]], i < m (fp32).
+ * poetx_dequant -- out[r][c] = bf16(scale * q[r][c]) for q int8 [rows][cols]
+ *   (cols % 16 == 0, 16-byte aligned); per_row = 1: scale[r] (q_f against
+ *   s_f gives W0f), per_row = 0: scale[c] (q_fT against s_f gives W0fT).
+ *   Rounds to nearest even.
+ * Errors: ERR_ARG, ERR_DEVICE.
+ */
+int32_t poetx_fold_scale(int32_t m, const float* s, const int32_t* perm_R, float* s_f,
+                         poetx_stream_t stream);
+int32_t poetx_dequant(int32_t rows, int32_t cols, const void* q, const float* scale,
+                      int32_t per_row, void* out, poetx_stream_t stream);
 
 /*
  * poetx_layer_fwd -- input-centric forward pass (technical summary 2.1-2.3).

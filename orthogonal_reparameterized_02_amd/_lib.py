@@ -11,6 +11,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpoetx.so")
 
 F32, BF16 = 0, 1
+I8 = 2  # weight storage only (fold, dequant)
 STATUS = {0: "POETX_OK", 1: "POETX_ERR_ARG", 2: "POETX_ERR_UNSUPPORTED",
           3: "POETX_ERR_WORKSPACE", 4: "POETX_ERR_DEVICE"}
 
@@ -33,6 +34,8 @@ SIGNATURES = {
                                   _p]),
     "poetx_saved_bytes_xmem": (_sz, [_p]),
     "poetx_merge": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "poetx_fold_scale": (_i, [_i, _p, _p, _p, _p]),
+    "poetx_dequant": (_i, [_i, _i, _p, _p, _i, _p, _p]),
     "poetx_set_stage_events": (_i, [_p, _i]),
 }
 

@@ -434,7 +434,8 @@ int32_t poetx_fold_perm(int32_t m, int32_t n, int32_t dt, const void* W0, const 
                         int32_t* perm_P_inv, poetx_stream_t stream) {
   const char* fn = "poetx_fold_perm";
   if (m < 1 || n < 1) return fail(POETX_ERR_ARG, "%s: m=%d n=%d must be >= 1", fn, m, n);
-  if (dt != POETX_F32 && dt != POETX_BF16) return fail(POETX_ERR_ARG, "%s: dtype %d", fn, dt);
+  if (dt != POETX_F32 && dt != POETX_BF16 && dt != POETX_I8)
+    return fail(POETX_ERR_ARG, "%s: dtype %d", fn, dt);
   NEED_PTR(W0);
   NEED_PTR(perm_R);
   NEED_PTR(perm_P);
@@ -442,8 +443,37 @@ int32_t poetx_fold_perm(int32_t m, int32_t n, int32_t dt, const void* W0, const 
   OPT_PTR(W0fT);
   OPT_PTR(perm_R_inv);
   OPT_PTR(perm_P_inv);
-  hipError_t e = launch_fold(m, n, (int)es_of(dt), W0, perm_R, perm_P, W0f, W0fT, perm_R_inv,
+  hipError_t e = launch_fold(m, n, dt == POETX_I8 ? 1 : (int)es_of(dt), W0, perm_R, perm_P, W0f, W0fT, perm_R_inv,
                              perm_P_inv, (hipStream_t)stream);
+  if (e != hipSuccess) return dev_fail(e, fn);
+  return ok();
+}
+
+int32_t poetx_fold_scale(int32_t m, const float* s, const int32_t* perm_R, float* s_f,
+                         poetx_stream_t stream) {
+  const char* fn = "poetx_fold_scale";
+  if (m < 1) return fail(POETX_ERR_ARG, "%s: m=%d must be >= 1", fn, m);
+  NEED_PTR(s);
+  NEED_PTR(perm_R);
+  NEED_PTR(s_f);
+  hipError_t e = launch_gather_f32(m, s, perm_R, s_f, (hipStream_t)stream);
+  if (e != hipSuccess) return dev_fail(e, fn);
+  return ok();
+}
+
+int32_t poetx_dequant(int32_t rows, int32_t cols, const void* q, const float* scale,
+                      int32_t per_row, void* out, poetx_stream_t stream) {
+  const char* fn = "poetx_dequant";
+  if (rows < 1 || cols < 1 || cols % 16)
+    return fail(POETX_ERR_ARG, "%s: rows=%d cols=%d (cols must be a positive multiple of 16)", fn,
+                rows, cols);
+  NEED_PTR(q);
+  NEED_PTR(scale);
+  NEED_PTR(out);
+  if ((uintptr_t)q % 16 || (uintptr_t)out % 16)
+    return fail(POETX_ERR_ARG, "%s: q and out must be 16-byte aligned", fn);
+  hipError_t e = launch_dequant_i8(rows, cols, (const int8_t*)q, scale, per_row ? 1 : 0,
+                                   (bf16*)out, (hipStream_t)stream);
   if (e != hipSuccess) return dev_fail(e, fn);
   return ok();
 }

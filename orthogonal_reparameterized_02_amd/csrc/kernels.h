@@ -19,7 +19,7 @@ __host__ __device__ inline float cnp_wcoef(int p, int k) {
   return ((p - 1) & 1) ? -cnp_coef(p, k) : cnp_coef(p, k);
 }
 
-// ---- permutations (perm.hip) ------------------------------------------
+// ---- permutations (perm.hip); es = element bytes 1 | 2 | 4 ----------------
 hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
                        const int32_t* pP, void* W0f, void* W0fT, int32_t* pRinv,
                        int32_t* pPinv, hipStream_t s);
@@ -32,6 +32,13 @@ hipError_t launch_permute_rows_cols(int rows, int width, int es, const void* in,
                                     hipStream_t s);
 // out[j][i] = in[i][j], in [m][n]
 hipError_t launch_transpose(int m, int n, int es, const void* in, void* out, hipStream_t s);
+// out = bf16(scale * q) for int8 q [rows][cols] (cols % 16 == 0); the scale
+// is indexed by row (per_row) or by column
+hipError_t launch_dequant_i8(long rows, int cols, const int8_t* q, const float* scale, int per_row,
+                             bf16* out, hipStream_t s);
+// dst[i] = src[idx[i]], i < n
+hipError_t launch_gather_f32(int n, const float* src, const int32_t* idx, float* dst,
+                             hipStream_t s);
 
 // ---- portable tiled kernels (simple.hip) ----------------------------------
 // C[bt][i][j] = sum_k A[bt][i][k] * B[bt][j][k]       (row-major, fp32 accumulate)

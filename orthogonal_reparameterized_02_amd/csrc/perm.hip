@@ -196,51 +196,90 @@ hipError_t permute_impl(int rows, int width, const void* in, const int32_t* rmap
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_permute_cols(int rows, int width, int es, const void* in, const int32_t* idx,
-                               void* out, hipStream_t s) {
-  if (rows <= 0 || width <= 0) return hipSuccess;
-  if (es == 2) return permute_impl<uint16_t>(rows, width, in, nullptr, idx, out, s);
-  return permute_impl<uint32_t>(rows, width, in, nullptr, idx, out, s);
+template <typename E>
+hipError_t transpose_impl(int m, int n, const void* in, void* out, hipStream_t s) {
+  dim3 grid((n + 31) / 32, (m + 31) / 32);
+  hipLaunchKernelGGL(k_transpose<E>, grid, dim3(256), 0, s, m, n, (const E*)in, (E*)out);
+  return hipGetLastError();
 }
 
+__global__ void k_gather_f32(int n, const float* __restrict__ src, const int32_t* __restrict__ idx,
+                             float* __restrict__ dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[idx[i]];
+}
+
+// out[r][c] = bf16(scale[r or c] * q[r][c]) for an int8 [rows][cols] matrix,
+// 16 elements per thread; the scale follows rows (per_row) or columns
+__global__ __launch_bounds__(256) void k_dequant_i8(long rows, int cols, const int8_t* __restrict__ q,
+                                                    const float* __restrict__ scale, int per_row,
+                                                    uint16_t* __restrict__ out) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const int vpr = cols / 16;
+  const long v = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (v >= rows * vpr) return;
+  const long r = v / vpr;
+  const int c0 = (int)(v % vpr) * 16;
+  const u32x4 in = *reinterpret_cast<const u32x4*>(q + r * cols + c0);
+  const int8_t* b = reinterpret_cast<const int8_t*>(&in);
+  uint32_t w[8];
+#pragma unroll
+  for (int e = 0; e < 16; e += 2) {
+    const float s0 = per_row ? scale[r] : scale[c0 + e];
+    const float s1 = per_row ? scale[r] : scale[c0 + e + 1];
+    w[e / 2] = pack2bf(s0 * (float)b[e], s1 * (float)b[e + 1]);
+  }
+  u32x4* o = reinterpret_cast<u32x4*>(out + r * cols + c0);
+  o[0] = (u32x4){w[0], w[1], w[2], w[3]};
+  o[1] = (u32x4){w[4], w[5], w[6], w[7]};
+}
+
+}  // namespace
+
+hipError_t launch_dequant_i8(long rows, int cols, const int8_t* q, const float* scale, int per_row,
+                             bf16* out, hipStream_t s) {
+  if (rows <= 0 || cols <= 0) return hipSuccess;
+  const long nv = rows * (cols / 16);
+  hipLaunchKernelGGL(k_dequant_i8, dim3((unsigned)((nv + 255) / 256)), dim3(256), 0, s, rows, cols,
+                     q, scale, per_row, out);
+  return hipGetLastError();
+}
+
+// element sizes: 1 (int8 weights), 2 (bf16), 4 (fp32)
 hipError_t launch_permute_rows_cols(int rows, int width, int es, const void* in,
                                     const int32_t* rmap, const int32_t* idx, void* out,
                                     hipStream_t s) {
   if (rows <= 0 || width <= 0) return hipSuccess;
+  if (es == 1) return permute_impl<uint8_t>(rows, width, in, rmap, idx, out, s);
   if (es == 2) return permute_impl<uint16_t>(rows, width, in, rmap, idx, out, s);
   return permute_impl<uint32_t>(rows, width, in, rmap, idx, out, s);
 }
 
+hipError_t launch_permute_cols(int rows, int width, int es, const void* in, const int32_t* idx,
+                               void* out, hipStream_t s) {
+  return launch_permute_rows_cols(rows, width, es, in, nullptr, idx, out, s);
+}
+
 hipError_t launch_transpose(int m, int n, int es, const void* in, void* out, hipStream_t s) {
   if (m <= 0 || n <= 0) return hipSuccess;
-  dim3 grid((n + 31) / 32, (m + 31) / 32);
-  if (es == 2)
-    hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, m, n, (const uint16_t*)in,
-                       (uint16_t*)out);
-  else
-    hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(256), 0, s, m, n, (const uint32_t*)in,
-                       (uint32_t*)out);
+  if (es == 1) return transpose_impl<uint8_t>(m, n, in, out, s);
+  if (es == 2) return transpose_impl<uint16_t>(m, n, in, out, s);
+  return transpose_impl<uint32_t>(m, n, in, out, s);
+}
+
+hipError_t launch_gather_f32(int n, const float* src, const int32_t* idx, float* dst,
+                             hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather_f32, dim3((n + 255) / 256), dim3(256), 0, s, n, src, idx, dst);
   return hipGetLastError();
 }
 
 hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
                        const int32_t* pP, void* W0f, void* W0fT, int32_t* pRinv,
                        int32_t* pPinv, hipStream_t s) {
-  hipError_t e = es == 2 ? permute_impl<uint16_t>(m, n, W0, pR, pP, W0f, s)
-                         : permute_impl<uint32_t>(m, n, W0, pR, pP, W0f, s);
+  hipError_t e = launch_permute_rows_cols(m, n, es, W0, pR, pP, W0f, s);
   if (e != hipSuccess) return e;
-  if (W0fT) {
-    dim3 grid((n + 31) / 32, (m + 31) / 32);
-    if (es == 2)
-      hipLaunchKernelGGL(k_transpose<uint16_t>, grid, dim3(256), 0, s, m, n,
-                         (const uint16_t*)W0f, (uint16_t*)W0fT);
-    else
-      hipLaunchKernelGGL(k_transpose<uint32_t>, grid, dim3(256), 0, s, m, n,
-                         (const uint32_t*)W0f, (uint32_t*)W0fT);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
+  if (W0fT && (e = launch_transpose(m, n, es, W0f, W0fT, s)) != hipSuccess) return e;
   if (pRinv) {
     hipLaunchKernelGGL(k_inverse_perm, dim3((m + 255) / 256), dim3(256), 0, s, m, pR, pRinv);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -137,3 +137,20 @@ def to_f64(storage: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16" or storage.dtype == np.uint16:
         return bf16_bits_to_f32(storage).astype(np.float64)
     return storage.astype(np.float64)
+
+
+def quantize_rows_int8(w: np.ndarray):
+    """An INT8 base weight as it would arrive for POET-XQ: symmetric per-row
+    quantization, s[i] = max_j |w[i, j]| / 127 (float32) and
+    q = round(w / s) clipped to [-127, 127] (int8).  The weight it represents
+    is s[:, None] * q, exactly representable in float64."""
+    w = np.asarray(w, dtype=np.float64)
+    s = (np.abs(w).max(axis=1) / 127.0).astype(np.float32)
+    s[s == 0] = 1.0
+    q = np.clip(np.rint(w / s.astype(np.float64)[:, None]), -127, 127).astype(np.int8)
+    return q, s
+
+
+def dequantized(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """The float64 weight an int8 (q, s) pair represents."""
+    return s.astype(np.float64)[:, None] * q.astype(np.float64)

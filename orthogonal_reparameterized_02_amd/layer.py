@@ -24,11 +24,16 @@ class POETXLayer:
     """Buffers and calls for one (m, n, b, k, T, dtype) layer."""
 
     def __init__(self, m: int, n: int, b: int, k: int, T: int, act: int, device="cuda",
-                 xmem: bool = False):
+                 xmem: bool = False, xq: bool = False):
         """xmem: keep only U for the backward pass and recompute Z there
-        (the memory-saving mode) instead of keeping U and Z."""
+        (the memory-saving mode) instead of keeping U and Z.
+        xq: the base weight is int8 with per-row scales (load_q); each pass
+        expands the folded int8 weight to bf16 in W0f / W0fT just before
+        the layer call (a multi-layer runtime would share those buffers)."""
         self.m, self.n, self.b, self.k, self.T, self.act = m, n, b, k, T, act
-        self.xmem = xmem
+        self.xmem, self.xq = xmem, xq
+        if xq and act != P.BF16:
+            raise ValueError("the int8 base weight is expanded to bf16: act must be BF16")
         self.sh = P.shape(m, n, b, k, T, act)
         dt = self.dtype = _DT[act]
         dev = self.device = torch.device(device)
@@ -36,6 +41,9 @@ class POETXLayer:
         self.nP, self.nR = nP, nR
         e = lambda *s, d=dt: torch.empty(*s, dtype=d, device=dev)
         self.W0f, self.W0fT = e(m, n), e(n, m)
+        if xq:
+            self.qf, self.qfT = e(m, n, d=torch.int8), e(n, m, d=torch.int8)
+            self.s_f = e(m, d=torch.float32)
         self.perm_P = e(n, d=torch.int32)
         self.perm_R = e(m, d=torch.int32)
         self.perm_P_inv = e(n, d=torch.int32)
@@ -87,6 +95,17 @@ class POETXLayer:
                       out, ws)
         return out
 
+    def load_q(self, q: torch.Tensor, s: torch.Tensor, theta_P: torch.Tensor,
+               theta_R: torch.Tensor, perm_P: torch.Tensor, perm_R: torch.Tensor) -> None:
+        """Set-up for an int8 base weight W0 = s[:, None] * q (xq layers)."""
+        assert self.xq
+        self.perm_P.copy_(perm_P)
+        self.perm_R.copy_(perm_R)
+        P.poetx_fold_perm(q.to(self.device, torch.int8).contiguous(), self.perm_R, self.perm_P,
+                          self.qf, self.qfT, self.perm_R_inv, self.perm_P_inv)
+        P.poetx_fold_scale(s.to(self.device, torch.float32).contiguous(), self.perm_R, self.s_f)
+        self.set_theta(theta_P, theta_R)
+
     def set_theta(self, theta_P: torch.Tensor, theta_R: torch.Tensor) -> None:
         self.theta_P.copy_(theta_P)
         self.theta_R.copy_(theta_R)
@@ -108,12 +127,16 @@ class POETXLayer:
 
     def layer_fwd(self, x: torch.Tensor) -> None:
         """The layer forward alone (G_P, G_R already formed)."""
+        if self.xq:
+            P.poetx_dequant(self.qf, self.s_f, True, self.W0f)
         fwd = P.poetx_layer_fwd_xmem if self.xmem else P.poetx_layer_fwd
         fwd(self.sh, x, self.G_P, self.G_R, self.W0f, self.perm_P, self.perm_R_inv, self.y,
             self.saved, self.ws_fwd)
 
     def layer_bwd(self, dy: torch.Tensor) -> None:
         """The layer backward alone (dx, dG_P, dG_R)."""
+        if self.xq:
+            P.poetx_dequant(self.qfT, self.s_f, False, self.W0fT)
         if self.xmem:
             P.poetx_layer_bwd_xmem(self.sh, dy, self.G_P, self.GT_P, self.GT_R, self.W0f,
                                    self.W0fT, self.perm_P_inv, self.perm_R, self.saved, self.dx,

@@ -13,7 +13,7 @@ from typing import Optional
 
 import torch
 
-from ._lib import BF16, F32, PoetxError, Shape, check, lib  # noqa: F401
+from ._lib import BF16, F32, I8, PoetxError, Shape, check, lib  # noqa: F401
 
 _DT = {F32: torch.float32, BF16: torch.bfloat16}
 
@@ -107,7 +107,7 @@ def poetx_fold_perm(W0: torch.Tensor, perm_R: torch.Tensor, perm_P: torch.Tensor
                     perm_R_inv: Optional[torch.Tensor] = None,
                     perm_P_inv: Optional[torch.Tensor] = None, stream=None) -> None:
     m, n = W0.shape
-    dt = act_of(W0.dtype)
+    dt = I8 if W0.dtype == torch.int8 else act_of(W0.dtype)
     check("poetx_fold_perm", lib().poetx_fold_perm(
         m, n, dt, _dev(W0, "W0"), _dev(perm_R, "perm_R", torch.int32, m),
         _dev(perm_P, "perm_P", torch.int32, n), _dev(W0f, "W0f", W0.dtype, m * n),
@@ -190,3 +190,20 @@ def poetx_merge(sh: Shape, W0f, G_R, GT_P, perm_R_inv, perm_P_inv, W0_out, ws,
         _dev(GT_P, "GT_P", dt, n * b), _dev(perm_R_inv, "perm_R_inv", torch.int32, m),
         _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(W0_out, "W0_out", dt, m * n),
         wp, wb, _stream(stream)))
+
+
+def poetx_fold_scale(s, perm_R, s_f, stream=None) -> None:
+    """s_f[i] = s[perm_R[i]] (the per-row scales of an int8 base weight)."""
+    m = perm_R.numel()
+    check("poetx_fold_scale", lib().poetx_fold_scale(
+        m, _dev(s, "s", torch.float32, m), _dev(perm_R, "perm_R", torch.int32, m),
+        _dev(s_f, "s_f", torch.float32, m), _stream(stream)))
+
+
+def poetx_dequant(q, scale, per_row: bool, out, stream=None) -> None:
+    """out = bf16(scale * q) for int8 q [rows][cols], scale by row or column."""
+    rows, cols = q.shape
+    check("poetx_dequant", lib().poetx_dequant(
+        rows, cols, _dev(q, "q", torch.int8, rows * cols),
+        _dev(scale, "scale", torch.float32, rows if per_row else cols), int(bool(per_row)),
+        _dev(out, "out", torch.bfloat16, rows * cols), _stream(stream)))

@@ -154,3 +154,13 @@ def test_merge_argument_errors():
     assert L.poetx_merge(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need,
                          None) == 1
     assert b"alias" in L.poetx_last_error()
+
+
+def test_xq_argument_errors():
+    L = _lib.lib()
+    assert L.poetx_dequant(64, 24, FAKE, FAKE, 1, FAKE, None) == 1      # cols % 16
+    assert L.poetx_dequant(64, 32, MISALIGNED, FAKE, 1, FAKE, None) == 1
+    assert L.poetx_dequant(64, 32, FAKE, None, 1, FAKE, None) == 1
+    assert L.poetx_fold_scale(0, FAKE, FAKE, FAKE, None) == 1
+    assert L.poetx_fold_scale(16, FAKE, None, FAKE, None) == 1
+    assert L.poetx_fold_perm(4, 4, 3, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == 1

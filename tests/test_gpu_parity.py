@@ -326,6 +326,84 @@ def test_end_inner_loop_keeps_the_function():
     assert err <= TOL["bf16"]
 
 
+# ------------------------------------------------------------------ POET-XQ
+def test_fold_int8_and_scales_bit_exact():
+    rng = np.random.default_rng(41)
+    m, n = 768, 512
+    q = rng.integers(-127, 128, size=(m, n)).astype(np.int8)
+    s = rng.uniform(0.001, 0.01, size=m).astype(np.float32)
+    pR, pP = rng.permutation(m).astype(np.int32), rng.permutation(n).astype(np.int32)
+    qf = torch.empty(m, n, dtype=torch.int8, device="cuda")
+    qfT = torch.empty(n, m, dtype=torch.int8, device="cuda")
+    sf = torch.empty(m, dtype=torch.float32, device="cuda")
+    P.poetx_fold_perm(to_dev(q), to_dev(pR), to_dev(pP), qf, qfT)
+    P.poetx_fold_scale(to_dev(s), to_dev(pR), sf)
+    torch.cuda.synchronize()
+    ref, _, _ = O.fold_perm(q, pR, pP)
+    np.testing.assert_array_equal(qf.cpu().numpy(), ref)
+    np.testing.assert_array_equal(qfT.cpu().numpy(), ref.T)
+    np.testing.assert_array_equal(sf.cpu().numpy(), s[pR])
+
+
+@pytest.mark.parametrize("per_row", [True, False])
+def test_dequant_bit_exact(per_row):
+    """bf16(s * q) with one float32 multiply and round-to-nearest-even."""
+    rng = np.random.default_rng(43)
+    rows, cols = 320, 448
+    q = rng.integers(-127, 128, size=(rows, cols)).astype(np.int8)
+    s = rng.uniform(1e-4, 1e-1, size=rows if per_row else cols).astype(np.float32)
+    out = torch.empty(rows, cols, dtype=torch.bfloat16, device="cuda")
+    P.poetx_dequant(to_dev(q), to_dev(s), per_row, out)
+    torch.cuda.synchronize()
+    sb = s[:, None] if per_row else s[None, :]
+    ref = I.bf16_round_bits((sb * q.astype(np.float32)).astype(np.float32))
+    np.testing.assert_array_equal(bits(out), ref)
+
+
+def _xq_layer(cfg, d, T):
+    q, sc = I.quantize_rows_int8(d["W064"])
+    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype), xq=True)
+    L.load_q(to_dev(q), to_dev(sc), to_dev(d["theta_P"]), to_dev(d["theta_R"]),
+             to_dev(d["perm_P"]), to_dev(d["perm_R"]))
+    L.step(to_dev(d["x"]), to_dev(d["dy"]))
+    torch.cuda.synchronize()
+    return L, I.dequantized(q, sc)
+
+
+@pytest.mark.parametrize("name,T", [("mid", 200), ("square", 96), ("mlp13b", 40)])
+def test_xq_layer_parity_small_T(name, T):
+    """The layer on an int8 base weight against the oracle on the weight the
+    int8 pair represents."""
+    cfg = I.CONFIG_BY_NAME[name]
+    say(f"xq {name} T={T}")
+    d = I.make_inputs(cfg, seed=45, T=T)
+    L, W0q = _xq_layer(cfg, d, T)
+    y_ref, _ = O.layer_fwd(d["x64"], W0q, d["theta_P64"], d["theta_R64"], d["perm_P"],
+                           d["perm_R"], cfg.b, cfg.k)
+    g = O.layer_bwd(d["x64"], d["dy64"], W0q, d["theta_P64"], d["theta_R64"], d["perm_P"],
+                    d["perm_R"], cfg.b, cfg.k)
+    errs = {"y": O.rel_fro(to_f64(L.y), y_ref), "dx": O.rel_fro(to_f64(L.dx), g["dx"]),
+            "dtheta_P": O.rel_fro(to_f64(L.dtheta_P), g["dtheta_P"]),
+            "dtheta_R": O.rel_fro(to_f64(L.dtheta_R), g["dtheta_R"])}
+    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOL[cfg.dtype], (k, v)
+
+
+def test_xq_layer_full_size():
+    cfg = I.CONFIG_BY_NAME["square"]
+    d = I.make_inputs(cfg, seed=0)
+    L, W0q = _xq_layer(cfg, d, cfg.T)
+    rows = np.sort(np.random.default_rng(3).choice(cfg.T, 32, replace=False))
+    G_P = O.cnp_fwd(d["theta_P64"], cfg.b, cfg.k)
+    G_R = O.cnp_fwd(d["theta_R64"], cfg.b, cfg.k)
+    W = O.weight(W0q, G_R, G_P, d["perm_R"], d["perm_P"])
+    e_y = O.rel_fro(to_f64(L.y[torch.as_tensor(rows, device="cuda")]), d["x64"][rows] @ W.T)
+    e_dx = O.rel_fro(to_f64(L.dx[torch.as_tensor(rows, device="cuda")]), d["dy64"][rows] @ W)
+    say(f"  xq full: y rows {e_y:.2e}  dx rows {e_dx:.2e}")
+    assert e_y <= TOL["bf16"] and e_dx <= TOL["bf16"]
+
+
 def test_autograd_module_matches_layer():
     from orthogonal_reparameterized_02_amd.layer import POETXLinear
     torch.manual_seed(0)

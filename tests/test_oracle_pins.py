@@ -281,3 +281,14 @@ def test_inputs_prefix_and_rounding():
     a[:4] = [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 0.0]      # ties
     t = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     np.testing.assert_array_equal(I.bf16_round_bits(a), t)
+
+
+def test_int8_base_weight_helper():
+    """The int8 base weight used for POET-XQ: per-row symmetric, every
+    element within half a quantization step of the weight it stands for."""
+    w = np.random.default_rng(9).standard_normal((64, 96)) * 0.05
+    q, s = I.quantize_rows_int8(w)
+    assert q.dtype == np.int8 and s.dtype == np.float32
+    assert np.abs(q).max() == 127 and q.min() >= -127
+    err = np.abs(I.dequantized(q, s) - w)
+    assert np.all(err <= s.astype(np.float64)[:, None] / 2 * (1 + 1e-6))
