@@ -42,7 +42,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="square")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--xmem", action="store_true",
                     help="memory-saving mode: keep only U, recompute Z in the backward")

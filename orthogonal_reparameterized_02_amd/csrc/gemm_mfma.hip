@@ -3,26 +3,26 @@
 // 2.3 batch-parallel blocks: each block is an independent matrix product,
 // the block-diagonal matrix is never built).
 //
-//   gemm_nt:  C[bt] = A[bt] B[bt]^T, A [M][K], B [N][K] (both K-contiguous),
-//             bf16 in, fp32 accumulate, bf16 out.  Serves Z = V W0f^T,
-//             dV = dZ W0f (B = W0f^T), and every per-token block product
-//             (A = a b-column slice of the activations, B = G or G^T).
-//             Optional block epilogue: when the output tile's 256 columns
-//             are exactly one b = 256 orthogonal block g, the tile also
-//             computes E = C_tile Bk_g^T (K = 256) from LDS and stores it, so
-//             Z -> S_i = Z_i G_Ri^T and dV -> dU_j = dV_j G_Pj leave the CU
-//             without a second pass over HBM.
-//   gemm_tn:  P[s][bt] = sum over a token range of A^T B, A [T][*] and
-//             B [T][*] token-major, fp32 partial sums (dG = dS^T Z and
-//             dG_P = dV^T U); a fixed-order reduction over s follows.
+//   k_nt4:      C = A B^T on 256 x 256 tiles, 4 waves, K fed by
+//               global_load_lds into four 32 KB stages (the dense products
+//               Z = V W0f^T and dV = dZ W0f, and large batched products).
+//               EPI 1 adds the block epilogue: when the tile's 256 columns
+//               are one b = 256 orthogonal block g, E = C_tile Bk_g^T
+//               (K = 256) is formed from the tile still in LDS, so
+//               Z -> S_i = Z_i G_Ri^T and dV -> dU_j = dV_j G_Pj leave the CU
+//               without a second pass over HBM.
+//   k_gemm_nt:  the same product with register-staged loads, for small or
+//               narrow shapes (fewer tiles than CUs, N % 256 != 0).
+//   k_blocks:   per-token block products with G_j resident in LDS
+//               (V = U G_P^T, dZ = dS G_R, b in {128, 256}).
+//   k_tn4 / k_gemm_tn: P[s][bt] = sum over a token range of A^T B, A [T][*]
+//               and B [T][*] token-major, fp32 partial sums (dG_R = dS^T Z,
+//               dG_P = dV^T U); a fixed-order reduction over s follows.
 //
-// Workgroups of WM x WN wave64s; tile BM x BN; K in slabs of 64 staged
-// through LDS (double buffered, one barrier per slab).  The 256 x 256 tile
-// runs 8 waves (two per SIMD) with 128 x 64 per wave, so one wave's LDS and
-// global-memory waits overlap the other's MFMAs.  LDS rows hold 64 bf16
-// (128 B) as eight 16-byte chunks, chunk c of row r stored at position
-// c ^ ((r ^ r/8) & 7): MFMA operand reads (16 rows, one chunk) and both the
-// row-wise (NT) and the transposing (TN) tile writes avoid bank conflicts.
+// LDS rows of 64 bf16 (128 B) hold eight 16-byte chunks, chunk c of row r
+// stored at position c ^ ((r ^ r/8) & 7); rows of 32 bf16 (64 B) use
+// c ^ ((r/2 ^ r/8) & 3).  Both keep the 16 rows an MFMA operand read
+// touches per phase on distinct banks.
 // MFMA: v_mfma_f32_32x32x16_bf16; lane l holds A[l%32][8*(l/32)+i] and
 // B[8*(l/32)+i][l%32]; acc[r] = D[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include <algorithm>
@@ -445,6 +445,161 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   }
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// two transposed 4 x 16 reads -> one 8-value MFMA operand
+__device__ __forceinline__ bf16x8_t frag_tr(const char* p0, const char* p1) {
+  const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p0)));
+  const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p1)));
+  const s16x8_t w = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// Token reduction P[s][bt][r][c] = sum over split s's tokens of
+// A[t][bt*sA + tr*TILE + r] * B[t][bt*sB + tc*TILE + c]  (dG = dS^T Z, dV^T U).
+// The k_nt4 pipeline with the operands' roles transposed: both operands are
+// token-major, so a K slab (32 tokens) lands in LDS as [token][feature]
+// rows (buffer_load ... lds: rows past the split's end read as zero), and
+// the MFMA fragments are read across tokens with ds_read_b64_tr_b16, which
+// hands lane i of each 16-lane group feature i of a 4-token x 16-feature
+// tile.  Two transposed reads give the eight consecutive tokens (K values) a
+// lane holds.  The 16-byte chunk index of a token row is XORed with
+// 2 * (token % 4), so the four rows one read touches fall on distinct banks.
+// Output: an fp32 TILE x TILE partial, staged through LDS for 16-byte stores.
+template <int TILE>
+__global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_tn4(
+    int T, int tsplit, int tiles1, const bf16* __restrict__ A, long lda, long sA,
+    const bf16* __restrict__ B, long ldb, long sB, float* __restrict__ P, long ldp, long sP, long sS) {
+  constexpr int WT = TILE / 2, FM = WT / 32, FN = WT / 32, NF = FM + FN;
+  constexpr int MPG = FM * FN / NF;               // MFMAs per group
+  constexpr int ROWB_T = TILE * 2;                // LDS bytes per token row
+  constexpr int A_BYTES = 32 * ROWB_T, STG = 2 * A_BYTES, NSTG = 4;
+  constexpr int NQ = STG / 1024 / 4;              // DMA instructions per wave per slab
+  static_assert(NQ == NF, "one DMA per group");
+  extern __shared__ __align__(16) char smem[];
+  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
+  const int wm = wave / 2, wn = wave % 2;
+  const int tr = blockIdx.x / tiles1, tc = blockIdx.x % tiles1;
+  const long bt = blockIdx.y;
+  const int s = blockIdx.z;
+  const int t_begin = s * tsplit, t_end = min(T, t_begin + tsplit);
+  P += s * sS + bt * sP;
+  const int ntok = max(0, t_end - t_begin);
+  const int nk = max(1, (ntok + 31) / 32);
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (long)t_begin * lda + bt * sA + tr * TILE), (short)0, ntok * (int)lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + (long)t_begin * ldb + bt * sB + tc * TILE), (short)0, ntok * (int)ldb * 2, 0x00020000);
+  int vo[NQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+    const int off = (q * 4 + wave) * 1024 + 16 * lane;
+    const int o = off % A_BYTES, row = o / ROWB_T, pc = (o % ROWB_T) / 16;
+    const int lc = pc ^ ((row & 3) << 1);
+    vo[q] = off < A_BYTES ? row * (int)lda * 2 + lc * 16 : row * (int)ldb * 2 + lc * 16;
+  }
+  const int slabA = 32 * (int)lda * 2, slabB = 32 * (int)ldb * 2;
+#define DMA1(slot, from, q)                                                                   \
+  {                                                                                           \
+    const uint32_t m0v_ = __builtin_amdgcn_readfirstlane(                                     \
+        lds0 + ((slot) % NSTG) * STG + ((q) * 4 + wave) * 1024);                              \
+    if ((q) * 4 < A_BYTES / 1024)                                                             \
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v_),  \
+                   "v"(vo[q] + (from) * slabA), "s"(rsA) : "memory", "m0");                   \
+    else                                                                                      \
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v_),  \
+                   "v"(vo[q] + (from) * slabB), "s"(rsB) : "memory", "m0");                   \
+  }
+  const int tk_l = 8 * (lane / 32) + (lane % 16) / 4;
+  const int ft_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#define FRAG(F, slab, ks, g)                                                                  \
+  {                                                                                           \
+    const char* S_ = smem + ((slab) % NSTG) * STG + ((g) < FM ? 0 : A_BYTES);                 \
+    const int ft_ = ((g) < FM ? wm * WT + (g) * 32 : wn * WT + ((g) - FM) * 32) + ft_l;        \
+    const int t0_ = 16 * (ks) + tk_l, t1_ = t0_ + 4;                                           \
+    const char* p0_ = S_ + t0_ * ROWB_T + (((ft_ >> 3) ^ ((t0_ & 3) << 1)) << 4) + (ft_ & 7) * 2; \
+    const char* p1_ = S_ + t1_ * ROWB_T + (((ft_ >> 3) ^ ((t1_ & 3) << 1)) << 4) + (ft_ & 7) * 2; \
+    if ((g) < FM) fa[F][(g)] = frag_tr(p0_, p1_);                                             \
+    else fb[F][(g) - FM] = frag_tr(p0_, p1_);                                                 \
+  }
+#define MMAG(F, g)                                                                            \
+  _Pragma("unroll") for (int u_ = 0; u_ < MPG; ++u_) {                                        \
+    const int m_ = (g) * MPG + u_;                                                            \
+    acc[m_ / FN][m_ % FN] = mfma32x32x16(fa[F][m_ / FN], fb[F][m_ % FN], acc[m_ / FN][m_ % FN]); \
+  }
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16_t){};
+  bf16x8_t fa[2][FM], fb[2][FN];
+#pragma unroll
+  for (int p = 0; p < NSTG; ++p)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) DMA1(p, min(p, nk - 1), q);
+  if constexpr (NQ == 8) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < NF; ++g) FRAG(0, 0, 0, g);
+  for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+    for (int g = 0; g < NF; ++g) {
+      FRAG(1, kt, 1, g);
+      MMAG(0, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (NQ == 8) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+    const int refill = min(kt + NSTG, nk - 1);
+#pragma unroll
+    for (int g = 0; g < NF; ++g) {
+      FRAG(0, kt + 1, 0, g);
+      MMAG(1, g);
+      DMA1(kt, refill, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#undef DMA1
+#undef FRAG
+#undef MMAG
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // fp32 tile out through LDS in passes of PR rows: [row][TILE] with the
+  // 16-byte chunk index XOR (row & 7), then 16-byte row stores
+  constexpr int PR = (NSTG * STG) / (TILE * 4) < TILE ? (NSTG * STG) / (TILE * 4) : TILE;
+  float* st = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int pass = 0; pass < TILE / PR; ++pass) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rb = wm * WT + i * 32;
+      if (rb < pass * PR || rb >= (pass + 1) * PR) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rb - pass * PR + acc_row(r, lane);
+          const int col = wn * WT + j * 32 + lane % 32;
+          st[row * TILE + (((col >> 2) ^ (row & 7)) << 2) + (col & 3)] = acc[i][j][r];
+        }
+    }
+    __syncthreads();
+    constexpr int CH = PR * TILE / 4;  // 16-byte chunks in the pass
+#pragma unroll
+    for (int u = 0; u < CH / 256; ++u) {
+      const int q = u * 256 + tid, row = q / (TILE / 4), c4 = q % (TILE / 4);
+      const float4 v = *reinterpret_cast<const float4*>(st + row * TILE + ((c4 ^ (row & 7)) << 2));
+      *reinterpret_cast<float4*>(P + (long)(tr * TILE + pass * PR + row) * ldp + tc * TILE + c4 * 4) = v;
+    }
+    __syncthreads();
+  }
+}
+
 // Partial token reduction: P[s][bt][r][c] = sum_{t in split s} A[t][r] B[t][c]
 // (A, B token-major, column offsets folded into the pointers per batch).
 template <int BT>
@@ -649,89 +804,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
   }
 }
 
-// 8 x 8 bf16 transpose within one thread: in[t] holds tokens t, features
-// 0..7 (two per dword); out[f] holds feature f, tokens 0..7
-__device__ __forceinline__ void transpose8x8(const uint4 (&in)[8], uint4 (&out)[8]) {
-  const uint32_t* w = reinterpret_cast<const uint32_t*>(in);  // w[t*4 + q]: features 2q, 2q+1
-  uint32_t* o = reinterpret_cast<uint32_t*>(out);              // o[f*4 + p]: tokens 2p, 2p+1
-#pragma unroll
-  for (int f = 0; f < 8; ++f)
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t lo = w[(2 * p) * 4 + f / 2], hi = w[(2 * p + 1) * 4 + f / 2];
-      o[f * 4 + p] = __builtin_amdgcn_perm(hi, lo, (f & 1) ? 0x07060302u : 0x05040100u);
-    }
-}
 
-// Partial token reduction over a whole 256 x 256 block per workgroup, 8 waves
-// (128 x 64 each): P[s][bt] = sum_{t in split s} A_bt^T B_bt.  Each thread
-// loads an 8-token x 8-feature piece of A or B, transposes it in registers
-// and writes 16-byte LDS rows [feature][token].
-__global__ __launch_bounds__(512, 1) void k_gemm_tn256(int T, int tsplit, const bf16* __restrict__ A,
-                                                       long lda, long sA, const bf16* __restrict__ B,
-                                                       long ldb, long sB, float* __restrict__ P,
-                                                       int tiles1, long sP, long sS) {
-  using C = Cfg<256, 256, 2, 4>;
-  extern __shared__ __align__(16) char smem[];
-  const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
-  const int wm = wave / 4, wn = wave % 4;
-  const int tile = blockIdx.x;  // (tm, tn) of 256-blocks inside a D x D block
-  const int tm = tile / tiles1, tn = tile % tiles1;
-  const long bt = blockIdx.y;
-  const int s = blockIdx.z;
-  const int t_begin = s * tsplit, t_end = min(T, t_begin + tsplit);
-  // this thread's piece: operand (A: tid < 256), token group tg, feature group fg
-  const int opnd = tid / 256, piece = tid % 256;
-  const int tg = piece / 32, fg = piece % 32;
-  const bf16* src = opnd == 0 ? A + bt * sA + tm * 256 : B + bt * sB + tn * 256;
-  const long ld = opnd == 0 ? lda : ldb;
-  uint4 rin[8];
-  auto gload = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int t = t0 + tg * 8 + i;
-      rin[i] = t < t_end ? *reinterpret_cast<const uint4*>(src + (long)t * ld + fg * 8) : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint4 rt[8];
-    transpose8x8(rin, rt);
-    char* base = smem + buf * C::STAGE + opnd * C::A_BYTES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(base + lds_off(fg * 8 + i, tg)) = rt[i];
-  };
-  f32x16_t acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x16_t){};
-  const int nk = (t_end - t_begin + BK - 1) / BK;
-  if (nk > 0) {
-    gload(t_begin);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(t_begin + (kt + 1) * BK);
-      const char* As = smem + cur * C::STAGE;
-      mma_slab<C>(As, As + C::A_BYTES, acc, wm, wn, lane);
-      if (kt + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
-    }
-  }
-  const int D = tiles1 * 256;
-  float* Pb = P + s * sS + bt * sP;
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = tm * 256 + wm * C::TM + i * 32 + acc_row(r, lane);
-        const int col = tn * 256 + wn * C::TN + j * 32 + lane % 32;
-        Pb[(long)row * D + col] = acc[i][j][r];
-      }
-}
 
 // out[e] = sum_{s < S} P[s * stride + e], fixed order
 __global__ void k_reduce_splits(long n, int S, long stride, const float* __restrict__ P,
@@ -862,7 +935,10 @@ hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, 
 int tn_splits(int batch, int D, int T) {
   const int BT = D >= 256 ? 256 : (D >= 128 ? 128 : 64);
   const long tiles = (long)batch * (D / BT) * (D / BT);
-  int S = (int)((NUM_CU + tiles - 1) / tiles);
+  // D >= 256 (k_tn4): half the CUs already saturate HBM there, and fewer
+  // splits mean fewer fp32 partials to write and reduce
+  const long want = D >= 256 ? NUM_CU / 2 : NUM_CU;
+  int S = (int)((want + tiles - 1) / tiles);
   const int max_s = (T + 255) / 256;  // keep >= 256 tokens per split
   S = S < max_s ? S : max_s;
   return S < 1 ? 1 : S;
@@ -880,13 +956,13 @@ hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long
   float* P = S > 1 ? partials : out;
   hipError_t e;
   if (D >= 256) {
-    static const hipError_t attr = set_lds(k_gemm_tn256, Cfg<256, 256, 2, 4>::LDS);
+    constexpr int lds = 4 * 2 * 32 * 256 * 2;  // four stages of 32 tokens x (A, B) rows
+    static const hipError_t attr = set_lds(k_tn4<256>, lds);
     if (attr != hipSuccess) return attr;
     const int tiles1 = D / 256;
-    const int tsplit = ((T + S - 1) / S + BK - 1) / BK * BK;
-    constexpr int lds = Cfg<256, 256, 2, 4>::LDS;
-    hipLaunchKernelGGL(k_gemm_tn256, dim3(tiles1 * tiles1, batch, S), dim3(512), lds, s, T, tsplit,
-                       A, lda, sA, B, ldb, sB, P, tiles1, dd, dd * batch);
+    const int tsplit = ((T + S - 1) / S + 31) / 32 * 32;
+    hipLaunchKernelGGL(k_tn4<256>, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit,
+                       tiles1, A, lda, sA, B, ldb, sB, P, (long)D, dd, dd * batch);
     e = hipGetLastError();
   } else if (D == 64) {
     e = tn_launch<64>(batch, D, T, S, A, lda, sA, B, ldb, sB, P, D, dd, dd * batch, s);
