@@ -152,6 +152,27 @@ def test_layer_parity_small_T(name):
         assert v <= TOL[cfg.dtype], (k, v)
 
 
+@pytest.mark.parametrize("name,T,k", [("square", 1, 4), ("square", 257, 4), ("mid", 33, 0),
+                                      ("mlp13b", 1, 5), ("probe", 1, 0)])
+def test_layer_edge_cases(name, T, k):
+    """One token, a ragged tail just past a 256-token tile, and k = 0
+    (G = I + Q): every output against the oracle."""
+    base = I.CONFIG_BY_NAME[name]
+    cfg = I.LayerConfig(base.name, base.m, base.n, base.b, k, T, base.dtype, base.sigma)
+    say(f"edge {name} T={T} k={k}")
+    d = I.make_inputs(cfg, seed=17, T=T)
+    L = run_layer(cfg, d, T)
+    y_ref, _ = O.layer_fwd(d["x64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
+                           d["perm_R"], cfg.b, cfg.k)
+    g = O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
+                    d["perm_R"], cfg.b, cfg.k)
+    for nm, got, ref in (("y", L.y, y_ref), ("dx", L.dx, g["dx"]),
+                         ("dtheta_P", L.dtheta_P, g["dtheta_P"]),
+                         ("dtheta_R", L.dtheta_R, g["dtheta_R"])):
+        err = O.rel_fro(to_f64(got), ref)
+        assert err <= TOL[cfg.dtype], (nm, err)
+
+
 @pytest.mark.parametrize("name", ["mid", "square", "mlp_up", "mlp13b"])
 def test_layer_parity_full_size(name):
     """Full token count, the launch configuration the bench times: sampled
