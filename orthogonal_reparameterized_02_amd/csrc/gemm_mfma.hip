@@ -315,14 +315,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     if (q < 4) src[q] = A + (long)min(m0 + r, M - 1) * lda + c * 8;
     else src[q] = B + (long)min(n0 + r - BM, N - 1) * ldb + c * 8;
   }
-  // DMA instruction q of this wave: slab `from` into the stage of slab `slot`
+  // DMA instruction q of this wave: slab `from` into the stage of slab `slot`.
+  // M0 (the LDS destination) is set inside the same asm statement; nothing
+  // else in these kernels reads M0 (no indirect register indexing, no LDS-DMA
+  // builtins), so the asm does not declare it.
 #define POETX_DMA1(slot, from, q)                                                              \
   {                                                                                            \
     const uint32_t m0v_ = __builtin_amdgcn_readfirstlane(                                      \
         lds0 + ((slot) % NSTG) * STG + ((q) * 4 + wave) * 16 * SROW);                          \
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v_),             \
                  "v"(src[q] + (long)(from) * SK)                                               \
-                 : "memory", "m0");                                                            \
+                 : "memory");                                                                 \
   }
   // operand fragment g of K-step ks of a slab: g < 4 reads A rows, else B rows
 #define POETX_FRAG(F, slab, ks, g)                                                             \
@@ -508,10 +511,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         lds0 + ((slot) % NSTG) * STG + ((q) * 4 + wave) * 1024);                              \
     if ((q) * 4 < A_BYTES / 1024)                                                             \
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v_),  \
-                   "v"(vo[q] + (from) * slabA), "s"(rsA) : "memory", "m0");                   \
+                   "v"(vo[q] + (from) * slabA), "s"(rsA) : "memory");                         \
     else                                                                                      \
       asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v_),  \
-                   "v"(vo[q] + (from) * slabB), "s"(rsB) : "memory", "m0");                   \
+                   "v"(vo[q] + (from) * slabB), "s"(rsB) : "memory");                         \
   }
   const int tk_l = 8 * (lane / 32) + (lane % 16) / 4;
   const int ft_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
