@@ -425,6 +425,36 @@ def test_xq_layer_full_size():
     assert e_y <= TOL["bf16"] and e_dx <= TOL["bf16"]
 
 
+def test_graph_replays_match_eager():
+    """The whole step captured as one HIP graph: every replay, with other
+    eager work and synchronizations in between, equals the eager step bit
+    for bit (the step records no memset nodes)."""
+    cfg = I.CONFIG_BY_NAME["square"]
+    T = 512
+    d = I.make_inputs(cfg, seed=51, T=T)
+    L = run_layer(cfg, d, T)
+    ref = [bits(t).copy() for t in (L.y, L.dx, L.dtheta_P, L.dtheta_R)]
+    other = run_layer(cfg, I.make_inputs(cfg, seed=52, T=T), T)
+    x, dy = to_dev(d["x"]), to_dev(d["dy"])
+    L.step(x, dy)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        L.step(x, dy)
+    torch.cuda.synchronize()
+    for i in range(3):
+        other.step(to_dev(I.make_inputs(cfg, seed=60 + i, T=T, want=("x",))["x"]),
+                   to_dev(d["dy"]))          # eager work between replays
+        torch.cuda.synchronize()
+        for t in (L.y, L.dx, L.dtheta_P, L.dtheta_R):
+            t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, t in zip(ref, (L.y, L.dx, L.dtheta_P, L.dtheta_R)):
+            np.testing.assert_array_equal(a, bits(t))
+
+
 def test_autograd_module_matches_layer():
     from orthogonal_reparameterized_02_amd.layer import POETXLinear
     torch.manual_seed(0)
