@@ -4,7 +4,7 @@
 // the block-diagonal matrix is never built).
 //
 //   k_nt4:      C = A B^T on 256 x 256 tiles, 4 waves, K fed by
-//               global_load_lds into four 32 KB stages (the dense products
+//               buffer_load ... lds into a ring of five 32 KB slots (the dense products
 //               Z = V W0f^T and dV = dZ W0f, and large batched products).
 //               EPI 1 adds the block epilogue: when the tile's 256 columns
 //               are one b = 256 orthogonal block g, E = C_tile Bk_g^T
@@ -20,9 +20,8 @@
 //               dG_P = dV^T U); a fixed-order reduction over s follows.
 //
 // LDS rows of 64 bf16 (128 B) hold eight 16-byte chunks, chunk c of row r
-// stored at position c ^ ((r ^ r/8) & 7); rows of 32 bf16 (64 B) use
-// c ^ ((r/2 ^ r/8) & 3).  Both keep the 16 rows an MFMA operand read
-// touches per phase on distinct banks.
+// stored at position c ^ ((r ^ r/8) & 7), which keeps the 16 rows an MFMA
+// operand read touches per phase on distinct banks.
 // MFMA: v_mfma_f32_32x32x16_bf16; lane l holds A[l%32][8*(l/32)+i] and
 // B[8*(l/32)+i][l%32]; acc[r] = D[8*(r/4) + 4*(l/32) + r%4][l%32].
 #include <algorithm>
@@ -264,35 +263,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
   }
 }
 
-// 64-byte LDS rows (K slabs of 32): 16-byte chunk c of row r sits at slot
-// c ^ ((r/2 ^ r/8) & 3), so the 16 rows one MFMA operand read touches per
-// phase fall on distinct banks.
-__device__ __forceinline__ int off32(int r, int c) {
-  return r * 64 + ((c ^ (((r >> 1) ^ (r >> 3)) & 3)) << 4);
-}
-
 // C = A B^T on a 256 x 256 tile with 4 waves (128 x 128 each, accumulators
-// in AGPRs).  K advances in slabs of 32 through NSTG = 4 LDS stages filled by
-// global_load_lds_dwordx4: the data go from L2 straight into LDS, so no
-// registers stage them and four slabs are in flight.  The DMA is issued from
-// inline asm (it has no register results) and its completion is tracked by
-// hand with vmcnt; the compiler therefore attaches no wait for it to the LDS
-// operand reads.  Each slab is two MFMA K-steps.  With one wave per SIMD,
-// nothing else hides a stall of the MFMA pipe, so the issue order is fixed
-// by hand (sched_barrier): every pair of MFMAs is followed by one operand
-// read for the next K-step and, in the second K-step, by one of the wave's
-// eight DMA instructions for the slab four ahead.  The one barrier per slab
-// sits between its two K-steps, where every wave has finished reading the
-// slab and the next one has landed.  EPI 1 adds the block epilogue of
-// k_gemm_nt.  Rows past M or N are clamped on load and masked on store.
+// in AGPRs).  K advances in slabs of 64: a slab row is 128 bytes, one whole
+// cache line, and eight lanes of a buffer_load_dwordx4 ... lds fetch it, so
+// every L2 request is a full line.  The data go from L2 straight into LDS
+// (no staging registers); the loads are issued from inline asm (they have no
+// register results) and completion is tracked by hand with vmcnt, so the
+// compiler puts no conservative wait in front of the LDS operand reads.
+// Operands live in a ring of five 32 KB slots (all 160 KB of LDS): slab j's
+// A rows in slot 2j mod 5, its B rows in slot 2j+1 mod 5.  While slab kt is
+// multiplied, slab kt+1 sits in two slots and A of slab kt+2 streams into the
+// fifth (during K-steps 0 and 1); B of slab kt+2 follows into A_kt's slot in
+// K-step 3, after the slab's one barrier, by which point every wave has
+// read slab kt (its last fragments are read during K-step 2).  With one wave
+// per SIMD nothing else hides a stall of the MFMA pipe, so the issue order
+// is fixed by hand (sched_barrier): each pair of MFMAs is followed by one
+// operand read for the next K-step and, where scheduled, one load.  Rows
+// past M or N read as zero through the buffer range check and are masked on
+// store.  The K order of the MFMAs is plain ascending, as in k_gemm_nt.
+// EPI 1 adds the block epilogue of k_gemm_nt.
 template <int EPI>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nt4(
     int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const bf16* __restrict__ B,
     long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN,
     const bf16* __restrict__ Bk, bf16* __restrict__ E, long lde) {
   constexpr int BM = 256, BN = 256, TM = 128, TN = 128, FM = 4, FN = 4, NTH = 256;
-  constexpr int NSTG = 4, SROW = 64, STG = (BM + BN) * SROW;  // 32 KB per stage
-  constexpr int SK = 32;                                      // K per slab
+  constexpr int OPB = 256 * ROWB;  // one operand's 256 rows of a 64-wide slab: 32 KB
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
@@ -300,44 +296,50 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   tile_of(blockIdx.x, gridDim.x, tilesM, tilesN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const long bt = blockIdx.y;
-  A += bt * sA;
-  B += bt * sB;
   Cm += bt * sC;
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
-  // DMA instruction q of this wave fills 16 rows (1 KB) of a stage: rows
-  // 0..255 hold A, 256..511 hold B.  Lane l lands at byte 16 l of the block,
-  // i.e. row l/4, slot l%4, so it fetches the logical chunk stored there.
-  const bf16* src[8];
+  // buffer ranges cover the tile's rows that exist (fewer than 256 at the
+  // bottom edge); offsets stay below 256 * ld * 2 < 2^31 (host-checked)
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + bt * sA + (long)m0 * lda), (short)0, min(BM, M - m0) * (int)lda * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(B + bt * sB + (long)n0 * ldb), (short)0, min(BN, N - n0) * (int)ldb * 2, 0x00020000);
+  // Load q (0..7) of this wave fills rows 32 q + 8 wave .. +7 of a slot
+  // (1 KB): lane l lands at byte 16 l, i.e. row 32 q + 8 wave + l/8, slot
+  // position l % 8, which holds logical chunk (l%8) ^ (l/8) ^ wave ^ 4 (q&1)
+  // under lds_off's swizzle.
+  const int rl = wave * 8 + lane / 8;
+  const int cx = (lane % 8) ^ (lane / 8) ^ wave;
+  int voA[2], voB[2];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int r = (q * 4 + wave) * 16 + lane / 4;
-    const int c = (lane % 4) ^ (((r >> 1) ^ (r >> 3)) & 3);
-    if (q < 4) src[q] = A + (long)min(m0 + r, M - 1) * lda + c * 8;
-    else src[q] = B + (long)min(n0 + r - BM, N - 1) * ldb + c * 8;
+  for (int p = 0; p < 2; ++p) {
+    voA[p] = rl * (int)lda * 2 + ((cx ^ (4 * p)) << 4);
+    voB[p] = rl * (int)ldb * 2 + ((cx ^ (4 * p)) << 4);
   }
-  // DMA instruction q of this wave: slab `from` into the stage of slab `slot`.
-  // M0 (the LDS destination) is set inside the same asm statement; nothing
-  // else in these kernels reads M0 (no indirect register indexing, no LDS-DMA
-  // builtins), so the asm does not declare it.
-#define POETX_DMA1(slot, from, q)                                                              \
+  const int gA = 32 * (int)lda * 2, gB = 32 * (int)ldb * 2;  // bytes per 32 rows
+  // load q of slab `from` into the slot at byte offset slotb.  M0 (the LDS
+  // destination) is set inside the same asm statement; nothing else in these
+  // kernels reads M0 (no indirect register indexing, no LDS-DMA builtins),
+  // so the asm does not declare it.
+#define POETX_DMA1(slotb, from, q, vo, g, rs)                                                  \
   {                                                                                            \
-    const uint32_t m0v_ = __builtin_amdgcn_readfirstlane(                                      \
-        lds0 + ((slot) % NSTG) * STG + ((q) * 4 + wave) * 16 * SROW);                          \
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0v_),             \
-                 "v"(src[q] + (long)(from) * SK)                                               \
+    const uint32_t m0v_ =                                                                      \
+        __builtin_amdgcn_readfirstlane(lds0 + (slotb) + ((q) * 4 + wave) * 1024);              \
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v_),    \
+                 "v"(vo[(q) & 1] + (q) * (g) + (from) * 128), "s"(rs)                          \
                  : "memory");                                                                 \
   }
-  // operand fragment g of K-step ks of a slab: g < 4 reads A rows, else B rows
-#define POETX_FRAG(F, slab, ks, g)                                                             \
+  // operand fragment g of K-step ks from slots sa (A) / sb (B): g < 4 reads A
+  // rows, else B rows
+#define POETX_FRAG(F, sa, sb, ks, g)                                                           \
   {                                                                                            \
-    const char* S_ = smem + ((slab) % NSTG) * STG;                                             \
     const int c_ = (ks) * 2 + lane / 32;                                                       \
     if ((g) < 4)                                                                               \
       fa[F][(g) & 3] = as_bf16x8(*reinterpret_cast<const uint4*>(                              \
-          S_ + off32(wm * TM + ((g) & 3) * 32 + lane % 32, c_)));                              \
+          smem + (sa) + lds_off(wm * TM + ((g) & 3) * 32 + lane % 32, c_)));                    \
     else                                                                                       \
       fb[F][(g) & 3] = as_bf16x8(*reinterpret_cast<const uint4*>(                              \
-          S_ + BM * SROW + off32(wn * TN + ((g) & 3) * 32 + lane % 32, c_)));                  \
+          smem + (sb) + lds_off(wn * TN + ((g) & 3) * 32 + lane % 32, c_)));                    \
   }
   // MFMAs 2g, 2g+1 of a K-step (row fragment g/2, column fragments 2(g%2)+{0,1})
 #define POETX_MMA2(F, g)                                                                       \
@@ -351,42 +353,67 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16_t){};
   bf16x8_t fa[2][FM], fb[2][FN];
-  const int nk = K / SK;
-  // Every stage is always filled: slab numbers past the end are clamped to
-  // the last slab, whose copy then lands in a stage that is never read.  So
-  // each wave always has exactly 8 DMA instructions per slab in flight and
-  // the vmcnt thresholds are constants.
+  const int nk = K / 64;
+  // Slab numbers past the end are clamped to the last slab; those copies land
+  // in slots that are never read again, so every wave always has the same
+  // number of loads in flight and the vmcnt thresholds are constants.
+  {
+    const int s1 = min(1, nk - 1);
 #pragma unroll
-  for (int p = 0; p < NSTG; ++p)
+    for (int q = 0; q < 8; ++q) POETX_DMA1(0 * OPB, 0, q, voA, gA, rsA);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) POETX_DMA1(p, min(p, nk - 1), q);
-  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");  // slab 0 has landed (this wave's part)
+    for (int q = 0; q < 8; ++q) POETX_DMA1(1 * OPB, 0, q, voB, gB, rsB);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) POETX_DMA1(2 * OPB, s1, q, voA, gA, rsA);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) POETX_DMA1(3 * OPB, s1, q, voB, gB, rsB);
+  }
+  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // slab 0 has landed (this wave's part)
   __syncthreads();
 #pragma unroll
-  for (int g = 0; g < 8; ++g) POETX_FRAG(0, 0, 0, g);
+  for (int g = 0; g < 8; ++g) POETX_FRAG(0, 0, OPB, 0, g);
+  int sl = 0;  // slot of A_kt (B_kt: sl+1, A_kt+1: sl+2, B_kt+1: sl+3, A_kt+2: sl+4, mod 5)
   for (int kt = 0; kt < nk; ++kt) {
-    // K-step 0 of slab kt; the fragments of K-step 1 are read in between
+    const int sa = sl * OPB, sb = (sl + 1 >= 5 ? sl - 4 : sl + 1) * OPB;
+    const int na = (sl + 2 >= 5 ? sl - 3 : sl + 2) * OPB, nb = (sl + 3 >= 5 ? sl - 2 : sl + 3) * OPB;
+    const int a2 = (sl + 4 >= 5 ? sl - 1 : sl + 4) * OPB;
+    const int pre = min(kt + 2, nk - 1);
+    // K-steps 0 and 1, each with the next K-step's fragments and half of A_kt+2
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      POETX_FRAG(1, kt, 1, g);
+      POETX_FRAG(1, sa, sb, 1, g);
+      POETX_MMA2(0, g);
+      if (g & 1) POETX_DMA1(a2, pre, g / 2, voA, gA, rsA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      POETX_FRAG(0, sa, sb, 2, g);
+      POETX_MMA2(1, g);
+      if (g & 1) POETX_DMA1(a2, pre, 4 + g / 2, voA, gA, rsA);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // K-step 2 with the last fragments of slab kt
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      POETX_FRAG(1, sa, sb, 3, g);
       POETX_MMA2(0, g);
       __builtin_amdgcn_sched_barrier(0);
     }
-    // slab kt+1 has landed when at most the two slabs after it are pending;
+    // slab kt+1 has landed when at most A_kt+2's eight loads are pending;
     // lgkmcnt(0): this wave's reads of slab kt are complete, so after the
-    // barrier slab kt's stage can be refilled
-    asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
+    // barrier A_kt's slot can be refilled
+    asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
     __syncthreads();
-    // K-step 1 of slab kt, with the first fragments of slab kt+1 and the
-    // DMA of slab kt+NSTG (into slab kt's stage) in between
-    const int refill = min(kt + NSTG, nk - 1);
+    // K-step 3, with slab kt+1's first fragments and B_kt+2 into A_kt's slot
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-      POETX_FRAG(0, kt + 1, 0, g);
+      POETX_FRAG(0, na, nb, 0, g);
       POETX_MMA2(1, g);
-      POETX_DMA1(kt, refill, g);
+      POETX_DMA1(sa, pre, g, voB, gB, rsB);
       __builtin_amdgcn_sched_barrier(0);
     }
+    sl = sl + 2 >= 5 ? sl - 3 : sl + 2;
   }
 #undef POETX_DMA1
 #undef POETX_FRAG
@@ -863,14 +890,17 @@ constexpr int NUM_CU = 256;
 
 bool mfma_nt_ok(int M, int N, int K) { return M > 0 && N % 64 == 0 && K % BK == 0; }
 
-// 4-wave 256 x 256 launcher; LDS: four 32 KB stages, or 160 KB for the
-// block epilogue's staged tile and G slab
+// k_nt4's buffer offsets reach 256 rows * ld * 2 bytes, kept below 2^31
+bool nt4_ld_ok(long lda, long ldb) { return lda > 0 && ldb > 0 && lda < (1L << 21) && ldb < (1L << 21); }
+
+// 4-wave 256 x 256 launcher; LDS: the five 32 KB operand slots (the block
+// epilogue stages its tile in the first 128 KB)
 template <int EPI>
 hipError_t nt4_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                       const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC, const bf16* Bk,
                       bf16* E, long lde, hipStream_t s) {
   auto kern = k_nt4<EPI>;
-  constexpr int lds = EPI == 1 ? (4 * 256 + 256) * ROWB : 4 * 512 * 64;
+  constexpr int lds = 5 * 256 * ROWB;
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
@@ -884,7 +914,7 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
                           hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return (long)batch * ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (N % 256 == 0 && tiles(256, 256) >= NUM_CU)
+  if (N % 256 == 0 && tiles(256, 256) >= NUM_CU && nt4_ld_ok(lda, ldb))
     return nt4_launch<0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, nullptr, nullptr, 0,
                          s);
   if (N % 128 == 0 && tiles(256, 128) >= NUM_CU)
@@ -898,12 +928,13 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
 }
 
 bool mfma_nt_block_ok(int M, int N, int K, int b) {
-  return b == 256 && N % 256 == 0 && K % BK == 0 && M > 0;
+  return b == 256 && N % 256 == 0 && K % BK == 0 && M > 0 && K < (1 << 21);
 }
 
 hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
                                 long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
                                 hipStream_t s) {
+  if (!nt4_ld_ok(lda, ldb)) return hipErrorInvalidValue;
   if (!E) return nt4_launch<0>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s);
   return nt4_launch<1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
 }
