@@ -341,12 +341,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       fb[F][(g) & 3] = as_bf16x8(*reinterpret_cast<const uint4*>(                              \
           smem + (sb) + lds_off(wn * TN + ((g) & 3) * 32 + lane % 32, c_)));                    \
   }
-  // MFMAs 2g, 2g+1 of a K-step (row fragment g/2, column fragments 2(g%2)+{0,1})
+  // MFMAs 2g, 2g+1 of a K-step: row fragment g/2 against two column
+  // fragments, which run 0..3 for even rows and 3..0 for odd ones, so that
+  // consecutive MFMAs change one operand (less switching power: the card is
+  // power-limited here).  Each accumulator still sums its K-steps in order.
 #define POETX_MMA2(F, g)                                                                       \
-  acc[(g) / 2][2 * ((g) % 2)] =                                                                \
-      mfma32x32x16(fa[F][(g) / 2], fb[F][2 * ((g) % 2)], acc[(g) / 2][2 * ((g) % 2)]);        \
-  acc[(g) / 2][2 * ((g) % 2) + 1] =                                                            \
-      mfma32x32x16(fa[F][(g) / 2], fb[F][2 * ((g) % 2) + 1], acc[(g) / 2][2 * ((g) % 2) + 1]);
+  {                                                                                            \
+    const int i_ = (g) / 2;                                                                    \
+    const int j0_ = (i_ & 1) ? 3 - 2 * ((g) % 2) : 2 * ((g) % 2);                              \
+    const int j1_ = (i_ & 1) ? j0_ - 1 : j0_ + 1;                                              \
+    acc[i_][j0_] = mfma32x32x16(fa[F][i_], fb[F][j0_], acc[i_][j0_]);                          \
+    acc[i_][j1_] = mfma32x32x16(fa[F][i_], fb[F][j1_], acc[i_][j1_]);                          \
+  }
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -465,7 +471,10 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32x32x16(ca[ks & 1][i], gb[ks % 3][j], acc[i][j]);
+        for (int jj = 0; jj < FN; ++jj) {
+          const int j = (i & 1) ? FN - 1 - jj : jj;  // one operand changes per MFMA
+          acc[i][j] = mfma32x32x16(ca[ks & 1][i], gb[ks % 3][j], acc[i][j]);
+        }
     }
 #undef POETX_CFRAG
     __syncthreads();  // every wave is done with the C tile
