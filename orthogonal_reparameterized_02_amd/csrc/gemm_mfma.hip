@@ -161,6 +161,56 @@ __device__ __forceinline__ void slabs_to_global(const char* lds, bf16* __restric
   }
 }
 
+// Transposed accumulator layout (k_nt4 swaps the MFMA operands): acc[i][j]
+// holds the 32 x 32 block of rows rbase + 32 i (lane l: row rbase + 32 i +
+// l % 32) and columns cbase + 32 j; register r holds column
+// 8 (r/4) + 4 (l/32) + r % 4 of it.  So four consecutive registers are four
+// consecutive columns of one row: one 8-byte LDS write per four values, into
+// the same [col/64][row][64] slab layout as acc_to_slabs.
+template <int FM, int FN>
+__device__ __forceinline__ void acc_to_slabsT(const f32x16_t (&acc)[FM][FN], char* lds, int slab_bytes,
+                                              int rbase, int cbase, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int row = rbase + i * 32 + (lane & 31);
+    const int key = (row ^ (row >> 3)) & 7;
+    char* rowp = lds + row * ROWB + 8 * h;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c0 = cbase + j * 32 + 8 * q;  // the lane's columns: c0 + 4 h .. + 3
+        uint2 v;
+        v.x = pack2bf(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        v.y = pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        *reinterpret_cast<uint2*>(rowp + (c0 >> 6) * slab_bytes + ((((c0 & 63) >> 3) ^ key) << 4)) = v;
+      }
+  }
+}
+
+// Slabs to global with buffer stores: rows past M fall outside the buffer
+// range and are dropped by the hardware, so there is no branch; every column
+// of the tile must exist (callers have N % COLS == 0).  Offsets stay below
+// ROWS * ldc * 2 < 2^31 (host-checked).
+template <int ROWS, int COLS, int NTH>
+__device__ __forceinline__ void slabs_to_global_buf(const char* lds, bf16* __restrict__ C, long ldc,
+                                                    int row0, int col0, int M) {
+  constexpr int CHUNKS = ROWS * COLS / 8, PER = CHUNKS / NTH, RSTEP = NTH / 8;
+  static_assert(CHUNKS % NTH == 0 && NTH % 8 == 0 && ROWS % RSTEP == 0, "store split");
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(C + (long)row0 * ldc + col0), (short)0, min(ROWS, M - row0) * (int)ldc * 2, 0x00020000);
+  const int c = threadIdx.x % 8, r0 = threadIdx.x / 8;
+  const int vbase = (r0 * (int)ldc + c * 8) * 2;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int s = u / (ROWS / RSTEP), ru = (u % (ROWS / RSTEP)) * RSTEP;
+    const u32x4v v = *reinterpret_cast<const u32x4v*>(lds + s * ROWS * ROWB + lds_off(ru + r0, c));
+    __builtin_amdgcn_raw_buffer_store_b128(v, rs, vbase + (ru * (int)ldc + s * 64) * 2, 0, 0);
+  }
+}
+
 // EPI: 0 plain store; 1 also E = C_tile * Bk_g^T for the tile's block g
 // (requires BN == 256 == block size, N-tile index = block index)
 template <int BM, int BN, int WM, int WN, int EPI>
@@ -345,13 +395,15 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // fragments, which run 0..3 for even rows and 3..0 for odd ones, so that
   // consecutive MFMAs change one operand (less switching power: the card is
   // power-limited here).  Each accumulator still sums its K-steps in order.
+  // The B fragment is the MFMA's first operand, so acc[i][j] holds its block
+  // transposed (acc_to_slabsT's layout).
 #define POETX_MMA2(F, g)                                                                       \
   {                                                                                            \
     const int i_ = (g) / 2;                                                                    \
     const int j0_ = (i_ & 1) ? 3 - 2 * ((g) % 2) : 2 * ((g) % 2);                              \
     const int j1_ = (i_ & 1) ? j0_ - 1 : j0_ + 1;                                              \
-    acc[i_][j0_] = mfma32x32x16(fa[F][i_], fb[F][j0_], acc[i_][j0_]);                          \
-    acc[i_][j1_] = mfma32x32x16(fa[F][i_], fb[F][j1_], acc[i_][j1_]);                          \
+    acc[i_][j0_] = mfma32x32x16(fb[F][j0_], fa[F][i_], acc[i_][j0_]);                          \
+    acc[i_][j1_] = mfma32x32x16(fb[F][j1_], fa[F][i_], acc[i_][j1_]);                          \
   }
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -428,11 +480,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   __syncthreads();
 
   constexpr int SLAB = BM * ROWB;
-  acc_to_slabs<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane, 0, BM);
-  // EPI 1: E = C_tile Bk_g^T, K = 256.  The A operand is the C tile just
-  // staged in LDS (four 64-wide K slabs); the B fragments come straight from
-  // global memory (the block's G is 128 KB and read by every tile of its
-  // column, so it sits in L2), two K-steps ahead, so the loop has no barrier.
+  acc_to_slabsT<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane);
+  // EPI 1: E = C_tile Bk_g^T, K = 256, formed transposed like C: the MFMA's
+  // first operand is a G fragment (rows of the block's G, straight from
+  // global memory: G is 128 KB and read by every tile of its column, so it
+  // sits in L2; two K-steps ahead, so the loop has no barrier), the second a
+  // fragment of the C tile just staged in LDS (four 64-wide K slabs).
   // The first loads go out before the C stores: vmcnt is in order, and a
   // wait for loads issued after the stores would wait for the stores too.
   const bf16* Gw = nullptr;
@@ -446,7 +499,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         gb[f][j] = as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * 256 + f * 16));
   }
   __syncthreads();
-  slabs_to_global<BM, BN, NTH>(smem, Cm, ldc, m0, n0, M, N);
+  slabs_to_global_buf<BM, BN, NTH>(smem, Cm, ldc, m0, n0, M);
   if constexpr (EPI == 1) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -473,14 +526,14 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
         for (int jj = 0; jj < FN; ++jj) {
           const int j = (i & 1) ? FN - 1 - jj : jj;  // one operand changes per MFMA
-          acc[i][j] = mfma32x32x16(ca[ks & 1][i], gb[ks % 3][j], acc[i][j]);
+          acc[i][j] = mfma32x32x16(gb[ks % 3][j], ca[ks & 1][i], acc[i][j]);
         }
     }
 #undef POETX_CFRAG
     __syncthreads();  // every wave is done with the C tile
-    acc_to_slabs<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane, 0, BM);
+    acc_to_slabsT<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane);
     __syncthreads();
-    slabs_to_global<BM, BN, NTH>(smem, E, lde, m0, n0, M, N);
+    slabs_to_global_buf<BM, BN, NTH>(smem, E, lde, m0, n0, M);
   }
 }
 
@@ -900,7 +953,9 @@ constexpr int NUM_CU = 256;
 bool mfma_nt_ok(int M, int N, int K) { return M > 0 && N % 64 == 0 && K % BK == 0; }
 
 // k_nt4's buffer offsets reach 256 rows * ld * 2 bytes, kept below 2^31
-bool nt4_ld_ok(long lda, long ldb) { return lda > 0 && ldb > 0 && lda < (1L << 21) && ldb < (1L << 21); }
+bool nt4_ld_ok(long lda, long ldb, long ldc) {
+  return lda > 0 && ldb > 0 && ldc > 0 && lda < (1L << 21) && ldb < (1L << 21) && ldc < (1L << 21);
+}
 
 // 4-wave 256 x 256 launcher; LDS: the five 32 KB operand slots (the block
 // epilogue stages its tile in the first 128 KB)
@@ -923,7 +978,7 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
                           hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return (long)batch * ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-  if (N % 256 == 0 && tiles(256, 256) >= NUM_CU && nt4_ld_ok(lda, ldb))
+  if (N % 256 == 0 && tiles(256, 256) >= NUM_CU && nt4_ld_ok(lda, ldb, ldc))
     return nt4_launch<0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, nullptr, nullptr, 0,
                          s);
   if (N % 128 == 0 && tiles(256, 128) >= NUM_CU)
@@ -943,7 +998,7 @@ bool mfma_nt_block_ok(int M, int N, int K, int b) {
 hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
                                 long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
                                 hipStream_t s) {
-  if (!nt4_ld_ok(lda, ldb)) return hipErrorInvalidValue;
+  if (!nt4_ld_ok(lda, ldb, ldc) || (E && !nt4_ld_ok(lda, ldb, lde))) return hipErrorInvalidValue;
   if (!E) return nt4_launch<0>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s);
   return nt4_launch<1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
 }
