@@ -192,22 +192,41 @@ __device__ __forceinline__ void acc_to_slabsT(const f32x16_t (&acc)[FM][FN], cha
 // Slabs to global with buffer stores: rows past M fall outside the buffer
 // range and are dropped by the hardware, so there is no branch; every column
 // of the tile must exist (callers have N % COLS == 0).  Offsets stay below
-// ROWS * ldc * 2 < 2^31 (host-checked).
+// ROWS * ldc * 2 < 2^31 (host-checked).  The range is clamped at zero rows:
+// a negative count would wrap to an unbounded range.
 template <int ROWS, int COLS, int NTH>
 __device__ __forceinline__ void slabs_to_global_buf(const char* lds, bf16* __restrict__ C, long ldc,
                                                     int row0, int col0, int M) {
-  constexpr int CHUNKS = ROWS * COLS / 8, PER = CHUNKS / NTH, RSTEP = NTH / 8;
-  static_assert(CHUNKS % NTH == 0 && NTH % 8 == 0 && ROWS % RSTEP == 0, "store split");
+  constexpr int CHUNKS = ROWS * COLS / 8;
+  static_assert(CHUNKS % NTH == 0 && (ROWS & (ROWS - 1)) == 0, "store split");
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+  // a pass may start at or past M (the last token tile of k_blocks): its
+  // range is then empty, not negative, and every store is dropped
+  // (base and count are uniform; readfirstlane keeps the resource in SGPRs)
+  const int nrows = __builtin_amdgcn_readfirstlane(max(0, min(ROWS, M - row0)));
+  const uint64_t base = (uint64_t)(uintptr_t)(C + (long)row0 * ldc + col0);
+  const uint64_t ubase = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(C + (long)row0 * ldc + col0), (short)0, min(ROWS, M - row0) * (int)ldc * 2, 0x00020000);
-  const int c = threadIdx.x % 8, r0 = threadIdx.x / 8;
-  const int vbase = (r0 * (int)ldc + c * 8) * 2;
+      (void*)(uintptr_t)ubase, (short)0, nrows * (int)ldc * 2, 0x00020000);
+  constexpr int RSTEP = NTH / 8;  // rows one pass of the workgroup covers
+  const int c = threadIdx.x % 8;
+  if constexpr (ROWS % RSTEP == 0) {  // each pass stays in one slab: offsets affine in u
+    const int r0 = threadIdx.x / 8, vbase = (r0 * (int)ldc + c * 8) * 2;
 #pragma unroll
-  for (int u = 0; u < PER; ++u) {
-    const int s = u / (ROWS / RSTEP), ru = (u % (ROWS / RSTEP)) * RSTEP;
-    const u32x4v v = *reinterpret_cast<const u32x4v*>(lds + s * ROWS * ROWB + lds_off(ru + r0, c));
-    __builtin_amdgcn_raw_buffer_store_b128(v, rs, vbase + (ru * (int)ldc + s * 64) * 2, 0, 0);
+    for (int u = 0; u < CHUNKS / NTH; ++u) {
+      const int s = u / (ROWS / RSTEP), ru = (u % (ROWS / RSTEP)) * RSTEP;
+      const u32x4v v = *reinterpret_cast<const u32x4v*>(lds + s * ROWS * ROWB + lds_off(ru + r0, c));
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, vbase + (ru * (int)ldc + s * 64) * 2, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < CHUNKS / NTH; ++u) {
+      const int q = u * NTH + threadIdx.x;
+      const int s = q / (ROWS * 8), r = (q >> 3) & (ROWS - 1);
+      const u32x4v v = *reinterpret_cast<const u32x4v*>(lds + s * ROWS * ROWB + lds_off(r, c));
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (r * (int)ldc + s * 64 + c * 8) * 2, 0, 0);
+    }
   }
 }
 
@@ -878,7 +897,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
             acc_to_slabs<FM, FN>(acc, stg, PROWS * ROWB, wm * TM, wn * TN, lane, p * PROWS,
                                  (p + 1) * PROWS);
             __syncthreads();
-            slabs_to_global<PROWS, B, NTH>(stg, Oj, width, t0 + p * PROWS, 0, T, B);
+            slabs_to_global_buf<PROWS, B, NTH>(stg, Oj, width, t0 + p * PROWS, 0, T);
             __syncthreads();
           }
 #pragma unroll
@@ -1024,6 +1043,7 @@ hipError_t blocks_launch(int nblk, int T, int width, const bf16* A, const bf16* 
 
 hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, const bf16* G,
                               bf16* Out, hipStream_t s) {
+  if (width <= 0 || width >= (1 << 21)) return hipErrorInvalidValue;  // 32-bit buffer offsets
   if (b == 256) return blocks_launch<256, 128, 2, 4>(nblk, T, width, A, G, Out, s);
   if (b == 128) return blocks_launch<128, 256, 4, 2>(nblk, T, width, A, G, Out, s);
   return hipErrorInvalidValue;
