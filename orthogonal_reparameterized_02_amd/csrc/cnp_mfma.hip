@@ -140,8 +140,16 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   bf16* Xs = reinterpret_cast<bf16*>(smem);         // [PW][QP]: X^T
   bf16* Qs = Xs + PW * QP;                          // [B][QP] (QLDS only)
 
-  const int J0 = blockIdx.x * PW;
-  const int blk = blockIdx.y;
+  // Workgroups are dealt round-robin over the 8 XCDs; renumber them so the
+  // panels of one block share an XCD, and so its L2 copy of Q (read by every
+  // panel) is fetched from MALL/HBM once instead of once per XCD.
+  int pan = blockIdx.x, blk = blockIdx.y;
+  if (gridDim.y % 8 == 0) {
+    const int id = blockIdx.y * gridDim.x + blockIdx.x, xcd = id % 8, slot = id / 8;
+    blk = xcd * (gridDim.y / 8) + slot / gridDim.x;
+    pan = slot % gridDim.x;
+  }
+  const int J0 = pan * PW;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
   const int col = lane % 32;
   const long boff = (long)blk * B * B;
