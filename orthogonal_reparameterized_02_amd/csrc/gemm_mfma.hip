@@ -8,7 +8,7 @@
 //               Z = V W0f^T and dV = dZ W0f, and large batched products).
 //               EPI 1 adds the block epilogue: when the tile's 256 columns
 //               are one b = 256 orthogonal block g, E = C_tile Bk_g^T
-//               (K = 256) is formed from the tile still in LDS, so
+//               (K = 256) is formed from the tile staged in LDS, so
 //               Z -> S_i = Z_i G_Ri^T and dV -> dU_j = dV_j G_Pj leave the CU
 //               without a second pass over HBM.
 //   k_gemm_nt:  the same product with register-staged loads, for small or
@@ -570,8 +570,10 @@ __device__ __forceinline__ bf16x8_t frag_tr(const char* p0, const char* p1) {
 
 // Token reduction P[s][bt][r][c] = sum over split s's tokens of
 // A[t][bt*sA + tr*TILE + r] * B[t][bt*sB + tc*TILE + c]  (dG = dS^T Z, dV^T U).
-// The k_nt4 pipeline with the operands' roles transposed: both operands are
-// token-major, so a K slab (32 tokens) lands in LDS as [token][feature]
+// A 4-wave, DMA-fed MFMA pipeline like k_nt4's (hand-fixed issue order, vmcnt
+// counted by hand), here with K slabs of 32 tokens in four 32 KB stages and
+// the operands' roles transposed: both operands are token-major, so a K
+// slab lands in LDS as [token][feature]
 // rows (buffer_load ... lds: rows past the split's end read as zero), and
 // the MFMA fragments are read across tokens with ds_read_b64_tr_b16, which
 // hands lane i of each 16-lane group feature i of a 4-token x 16-feature
