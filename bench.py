@@ -110,18 +110,19 @@ def main() -> int:
         run_step = graph.replay
 
     # ---- timed region: exactly K steps -----------------------------------
+    # (an event between consecutive steps as well, for the per-step spread)
     stream = torch.cuda.current_stream()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         run_step()
-    t1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    ms = t0.elapsed_time(t1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])
 
     # ---- per-stage times: the same K steps again with boundary events ----
     # (events are recorded on the stream the kernels run on)
@@ -205,6 +206,7 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        "ms_per_step_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
