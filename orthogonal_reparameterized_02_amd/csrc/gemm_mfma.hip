@@ -230,13 +230,12 @@ __device__ __forceinline__ void slabs_to_global_buf(const char* lds, bf16* __res
   }
 }
 
-// EPI: 0 plain store; 1 also E = C_tile * Bk_g^T for the tile's block g
-// (requires BN == 256 == block size, N-tile index = block index)
-template <int BM, int BN, int WM, int WN, int EPI>
+// C = A B^T with register-staged loads (two LDS stages), for shapes k_nt4
+// does not take: fewer 256 x 256 tiles than CUs, or N % 256 != 0.
+template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
     int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const bf16* __restrict__ B,
-    long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN,
-    const bf16* __restrict__ Bk, bf16* __restrict__ E, long lde) {
+    long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN) {
   using C = Cfg<BM, BN, WM, WN>;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -298,38 +297,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
   acc_to_slabs<C::FM, C::FN>(acc, smem, SLAB, wm * C::TM, wn * C::TN, lane, 0, BM);
   __syncthreads();
   slabs_to_global<BM, BN, C::NTH>(smem, Cm, ldc, m0, n0, M, N);
-  if constexpr (EPI == 1) {
-    static_assert(BN == 256 && BN % BK == 0, "block epilogue needs a 256-column tile");
-    // the C tile now sits in LDS as four K-slabs of 64 columns: the A operand
-    // of E[row][n] = sum_k Ct[row][k] Bk[g][n][k].  The block's G slab
-    // [256 n][64 k] is staged in the 32 KB above it, the next slab's loads in
-    // flight during the current slab's MFMAs.
-    const bf16* Bg = Bk + (long)tn * 256 * 256;
-    char* Gs = smem + 4 * SLAB;
-    constexpr int GP = 256 / C::RPP;  // 16-byte loads per thread per slab
-    uint4 gq[GP];
-    auto gfetch = [&](int ks) {
-#pragma unroll
-      for (int p = 0; p < GP; ++p)
-        gq[p] = *reinterpret_cast<const uint4*>(Bg + (long)(p * C::RPP + lr) * 256 + ks * BK + lc * 8);
-    };
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j) acc[i][j] = (f32x16_t){};
-    gfetch(0);
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int p = 0; p < GP; ++p) *reinterpret_cast<uint4*>(Gs + lds_off(p * C::RPP + lr, lc)) = gq[p];
-      __syncthreads();  // G slab visible
-      if (ks + 1 < 4) gfetch(ks + 1);
-      mma_slab<C>(smem + ks * SLAB, Gs, acc, wm, wn, lane);
-      __syncthreads();  // every wave is done with this G slab (and, at the end, the C tile)
-    }
-    acc_to_slabs<C::FM, C::FN>(acc, smem, SLAB, wm * C::TM, wn * C::TN, lane, 0, BM);
-    __syncthreads();
-    slabs_to_global<BM, BN, C::NTH>(smem, E, lde, m0, n0, M, N);
-  }
 }
 
 // C = A B^T on a 256 x 256 tile with 4 waves (128 x 128 each, accumulators
@@ -349,8 +316,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
 // is fixed by hand (sched_barrier): each pair of MFMAs is followed by one
 // operand read for the next K-step and, where scheduled, one load.  Rows
 // past M or N read as zero through the buffer range check and are masked on
-// store.  The K order of the MFMAs is plain ascending, as in k_gemm_nt.
-// EPI 1 adds the block epilogue of k_gemm_nt.
+// store (buffer stores whose range covers the tile's existing rows).  The K
+// order of the MFMAs is plain ascending, as in k_gemm_nt.  EPI 1 adds the
+// block epilogue (described at its code below).
 template <int EPI>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nt4(
     int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const bf16* __restrict__ B,
@@ -935,20 +903,18 @@ hipError_t set_lds(K kern, int bytes) {
   return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN>
 hipError_t nt_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA, const bf16* B,
-                     long ldb, long sB, bf16* C, long ldc, long sC, const bf16* Bk, bf16* E,
-                     long lde, hipStream_t s) {
+                     long ldb, long sB, bf16* C, long ldc, long sC, hipStream_t s) {
   using CF = Cfg<BM, BN, WM, WN>;
-  auto kern = k_gemm_nt<BM, BN, WM, WN, EPI>;
-  // the block epilogue keeps the C tile (4 slabs) plus one 256 x 64 G slab
-  constexpr int lds = EPI == 1 ? (4 * BM + 256) * ROWB : CF::LDS;
+  auto kern = k_gemm_nt<BM, BN, WM, WN>;
+  constexpr int lds = CF::LDS;
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
   hipLaunchKernelGGL(kern, dim3(tilesM * tilesN, batch), dim3(CF::NTH), lds, s, M, N, K, A, lda,
-                     sA, B, ldb, sB, C, ldc, sC, tilesM, tilesN, Bk, E, lde);
+                     sA, B, ldb, sB, C, ldc, sC, tilesM, tilesN);
   return hipGetLastError();
 }
 
@@ -1003,13 +969,10 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
     return nt4_launch<0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, nullptr, nullptr, 0,
                          s);
   if (N % 128 == 0 && tiles(256, 128) >= NUM_CU)
-    return nt_launch<256, 128, 2, 2, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
-                                        nullptr, nullptr, 0, s);
+    return nt_launch<256, 128, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
   if (N % 128 == 0)
-    return nt_launch<128, 128, 2, 2, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC,
-                                        nullptr, nullptr, 0, s);
-  return nt_launch<128, 64, 2, 2, 0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, nullptr,
-                                     nullptr, 0, s);
+    return nt_launch<128, 128, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+  return nt_launch<128, 64, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
 }
 
 bool mfma_nt_block_ok(int M, int N, int K, int b) {
