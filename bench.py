@@ -57,9 +57,9 @@ def main() -> int:
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the layer would shard over tokens with one all-reduce of the packed "
-              "gradients, which is not built here)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the layer "
+              "would shard over tokens with one all-reduce of the packed gradients; that "
+              "multi-GPU path is not implemented)", file=sys.stderr)
         return 2
 
     import numpy as np

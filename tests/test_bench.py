@@ -1,0 +1,43 @@
+"""Host-side checks of bench.py: the refusal of more than one GPU, the flop
+accounting it reports peak fractions against, and the CPU-baseline leg (the
+float64 oracle) on the small fp32 workload."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from orthogonal_reparameterized_02_amd import inputs as I  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""  # no JSON line
+
+
+@pytest.mark.parametrize("name, gflop", [("probe", 0.0357), ("mid", 83.21), ("square", 665.72),
+                                         ("mlp_up", 4341.1), ("mlp13b", 2945.0)])
+def test_step_flops(name, gflop):
+    # per token 2mn (Z) + 2mn (dV) + 2b(n + m) forward blocks + 4b(n + m)
+    # backward blocks and reductions; per step 2k b^3 (forward) + 4k b^3
+    # (backward) per block over (m + n) / b blocks
+    cfg = I.CONFIG_BY_NAME[name]
+    m, n, b, k, T = cfg.m, cfg.n, cfg.b, cfg.k, cfg.T
+    by_parts = T * (2 * m * n + 2 * m * n + 2 * b * (m + n) + 4 * b * (m + n)) \
+        + (2 * k * b ** 3 + 4 * k * b ** 3) * ((m + n) // b)
+    assert bench.step_flops(cfg) == pytest.approx(by_parts, rel=1e-12)
+    assert bench.step_flops(cfg) / 1e9 == pytest.approx(gflop, rel=2e-3)
+
+
+def test_cpu_baseline_is_the_oracle():
+    r = bench.cpu_baseline(I.CONFIG_BY_NAME["probe"], 0, 64, min_s=0.0, max_reps=1)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert "64 of 64 tokens" in r["sample"]
