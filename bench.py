@@ -224,7 +224,7 @@ def main() -> int:
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
         "inner_loop_merge_us": round(merge_us, 2),
         "roofline": {"kernel": ("k_nt4<1>: Z = V W0f^T with S = Z G_R^T "
-                                "in the epilogue" if fused else "k_gemm_nt: Z = V W0f^T"),
+                                "in the epilogue" if fused else f"{unfused_dense_kernel(T, m)}: Z = V W0f^T"),
                      "bound": "mfma", "achieved": dense_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": dense_tflops / peak,
                      "traffic": measured_traffic(cfg.name) if fused else None,
@@ -242,6 +242,13 @@ def main() -> int:
 COPY_PROBE_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_nt4_block_square_traffic.md")
 KERNEL_SOURCE = os.path.join(ROOT, "orthogonal_reparameterized_02_amd", "csrc", "gemm_mfma.hip")
+
+
+def unfused_dense_kernel(T, m):
+    """The kernel the library picks for the unfused Z = V W0f^T (T x m output):
+    the 256 x 256 one from half a tile per CU up, the 256 x 128 one below."""
+    tiles = -(-T // 256) * -(-m // 256)
+    return "k_nt4<0>" if m % 256 == 0 and tiles >= 128 else "k_gemm_nt"
 
 
 def measured_traffic(config_name: str):
