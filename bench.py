@@ -191,9 +191,9 @@ def main() -> int:
     peak = PEAK_BF16_TFLOPS if act == P.BF16 else PEAK_FP32_TFLOPS
     tokens_per_s = T / (ms * 1e-3)
     dense_us = stages["dense_Z"]
-    # b = 256 in bf16: the dense kernel also forms S = Z G_R^T per block in its
-    # epilogue (the library's fused path), 2 m b flops per token more
-    fused = act == P.BF16 and b == 256 and m % 256 == 0 and n % 64 == 0
+    # b = 256 or 128 in bf16: the dense kernel also forms S = Z G_R^T per block
+    # in its epilogue (the library's fused path), 2 m b flops per token more
+    fused = act == P.BF16 and b in (128, 256) and m % 256 == 0 and n % 64 == 0
     dense_flops = 2.0 * T * m * n + (2.0 * T * m * b if fused else 0.0)
     dense_tflops = dense_flops / (dense_us * 1e-6) / 1e12
     nblocks = cfg.n_P + cfg.n_R
@@ -223,7 +223,7 @@ def main() -> int:
                              "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
         "inner_loop_merge_us": round(merge_us, 2),
-        "roofline": {"kernel": ("k_nt4<1>: Z = V W0f^T with S = Z G_R^T "
+        "roofline": {"kernel": (f"k_nt4<{1 if b == 256 else 2}>: Z = V W0f^T with S = Z G_R^T "
                                 "in the epilogue" if fused else f"{unfused_dense_kernel(T, m)}: Z = V W0f^T"),
                      "bound": "mfma", "achieved": dense_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": dense_tflops / peak,

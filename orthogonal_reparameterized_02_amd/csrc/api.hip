@@ -214,8 +214,8 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
   mark(2, s);
   if constexpr (sizeof(TS) == 2) {
     if (mf && mfma_nt_block_ok(T, m, n, b)) {
-      // Z = V W0f^T and, per 256-column tile, S_i = Z_i G_Ri^T in one kernel
-      if ((e = launch_mfma_nt_block(T, m, n, V, n, W0f, n, Z, m, G_R, S, m, s)) != hipSuccess)
+      // Z = V W0f^T and, per output block, S_i = Z_i G_Ri^T in one kernel
+      if ((e = launch_mfma_nt_block(T, m, n, b, V, n, W0f, n, Z, m, G_R, S, m, s)) != hipSuccess)
         return dev_fail(e, "W0 product + R-side blocks");
       mark(3, s);
       mark(4, s);
@@ -267,7 +267,7 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
     bool done = false;
     if constexpr (sizeof(TS) == 2) {
       if (mf && mfma_nt_block_ok(T, m, n, b)) {
-        if ((e = launch_mfma_nt_block(T, m, n, V, n, W0f, n, Zr, m, nullptr, nullptr, 0, s)) !=
+        if ((e = launch_mfma_nt_block(T, m, n, b, V, n, W0f, n, Zr, m, nullptr, nullptr, 0, s)) !=
             hipSuccess)
           return dev_fail(e, "recompute Z");
         done = true;
@@ -295,8 +295,8 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
     bool fused = false;
     if constexpr (sizeof(TS) == 2) {
       if (mf && mfma_nt_block_ok(T, n, m, b)) {
-        // dV = dZ W0f and, per 256-column tile, dU_j = dV_j G_Pj in one kernel
-        if ((e = launch_mfma_nt_block(T, n, m, dZ, m, W0fT, m, dV, n, GT_P, dU, n, s)) != hipSuccess)
+        // dV = dZ W0f and, per input block, dU_j = dV_j G_Pj in one kernel
+        if ((e = launch_mfma_nt_block(T, n, m, b, dZ, m, W0fT, m, dV, n, GT_P, dU, n, s)) != hipSuccess)
           return dev_fail(e, "W0 product + P-side blocks (bwd)");
         mark(4, s);
         fused = true;

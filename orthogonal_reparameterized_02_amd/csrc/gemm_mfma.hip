@@ -6,11 +6,12 @@
 //   k_nt4:      C = A B^T on 256 x 256 tiles, 4 waves, K fed by
 //               buffer_load ... lds into a ring of five 32 KB slots (the dense products
 //               Z = V W0f^T and dV = dZ W0f, and large batched products).
-//               EPI 1 adds the block epilogue: when the tile's 256 columns
-//               are one b = 256 orthogonal block g, E = C_tile Bk_g^T
-//               (K = 256) is formed from the tile staged in LDS, so
-//               Z -> S_i = Z_i G_Ri^T and dV -> dU_j = dV_j G_Pj leave the CU
-//               without a second pass over HBM.
+//               EPI 1 and 2 add the block epilogue: when the tile's 256
+//               columns are one b = 256 orthogonal block g (EPI 1) or two
+//               b = 128 blocks (EPI 2), E = C_tile blockdiag(Bk)^T is formed
+//               from the tile staged in LDS, so Z -> S_i = Z_i G_Ri^T and
+//               dV -> dU_j = dV_j G_Pj leave the CU without a second pass
+//               over HBM.
 //   k_gemm_nt:  the same product with register-staged loads, for small or
 //               narrow shapes (fewer tiles than CUs, N % 256 != 0).
 //   k_blocks:   per-token block products with G_j resident in LDS
@@ -468,26 +469,35 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
   constexpr int SLAB = BM * ROWB;
   acc_to_slabsT<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane);
-  // EPI 1: E = C_tile Bk_g^T, K = 256, formed transposed like C: the MFMA's
-  // first operand is a G fragment (rows of the block's G, straight from
-  // global memory: G is 128 KB and read by every tile of its column, so it
-  // sits in L2; two K-steps ahead, so the loop has no barrier), the second a
-  // fragment of the C tile just staged in LDS (four 64-wide K slabs).
-  // The first loads go out before the C stores: vmcnt is in order, and a
-  // wait for loads issued after the stores would wait for the stores too.
+  // Block epilogue, E = C_tile blockdiag(G)^T, formed transposed like C.
+  // EPI 1 (blocks of 256): the tile's columns are one block, so every wave
+  // sums over all 256 columns of the C tile with G block tn.  EPI 2 (blocks
+  // of 128): a wave's 128 output columns (half wn of the tile) are exactly
+  // block 2 tn + wn, so it sums over that half of the C tile only.  The
+  // MFMA's first operand is a G fragment (rows of the block's G, straight
+  // from global memory: G is read by every tile of its column, so it sits in
+  // L2; two K-steps ahead, so the loop has no barrier), the second a fragment
+  // of the C tile just staged in LDS (four 64-wide K slabs).  The first loads
+  // go out before the C stores: vmcnt is in order, and a wait for loads
+  // issued after the stores would wait for the stores too.
+  constexpr int EB = EPI == 2 ? 128 : 256;  // block size
+  constexpr int EKS = EB / 16;               // K-steps of the block product
+  const int ek0 = EPI == 2 ? wn * 8 : 0;     // first K-step within the C tile
   const bf16* Gw = nullptr;
   bf16x8_t gb[3][FN];
-  if constexpr (EPI == 1) {
-    Gw = Bk + (long)tn * 256 * 256 + (long)(wn * TN + lane % 32) * 256 + 8 * (lane / 32);
+  if constexpr (EPI != 0) {
+    const long gblk = EPI == 2 ? 2L * tn + wn : (long)tn;
+    const int grow = EPI == 2 ? lane % 32 : wn * TN + lane % 32;
+    Gw = Bk + gblk * EB * EB + (long)grow * EB + 8 * (lane / 32);
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        gb[f][j] = as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * 256 + f * 16));
+        gb[f][j] = as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * EB + f * 16));
   }
   __syncthreads();
   slabs_to_global_buf<BM, BN, NTH>(smem, Cm, ldc, m0, n0, M);
-  if constexpr (EPI == 1) {
+  if constexpr (EPI != 0) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -495,19 +505,19 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     bf16x8_t ca[2][FM];
 #define POETX_CFRAG(F, ks)                                                                     \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) ca[F][i] = as_bf16x8(                       \
-        *reinterpret_cast<const uint4*>(smem + ((ks) / 4) * SLAB +                             \
+        *reinterpret_cast<const uint4*>(smem + ((ek0 + (ks)) / 4) * SLAB +                     \
                                         lds_off(wm * TM + i * 32 + lane % 32,                  \
                                                 ((ks) % 4) * 2 + lane / 32)));
     POETX_CFRAG(0, 0);
 #pragma unroll
-    for (int ks = 0; ks < 16; ++ks) {
-      if (ks + 2 < 16) {
+    for (int ks = 0; ks < EKS; ++ks) {
+      if (ks + 2 < EKS) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           gb[(ks + 2) % 3][j] =
-              as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * 256 + (ks + 2) * 16));
+              as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * EB + (ks + 2) * 16));
       }
-      if (ks + 1 < 16) { POETX_CFRAG((ks + 1) & 1, ks + 1); }
+      if (ks + 1 < EKS) { POETX_CFRAG((ks + 1) & 1, ks + 1); }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -978,14 +988,16 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
 }
 
 bool mfma_nt_block_ok(int M, int N, int K, int b) {
-  return b == 256 && N % 256 == 0 && K % BK == 0 && M > 0 && K < (1 << 21);
+  return (b == 256 || b == 128) && N % 256 == 0 && K % BK == 0 && M > 0 && K < (1 << 21);
 }
 
-hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
-                                long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
-                                hipStream_t s) {
+hipError_t launch_mfma_nt_block(int M, int N, int K, int b, const bf16* A, long lda,
+                                const bf16* B, long ldb, bf16* C, long ldc, const bf16* Bk,
+                                bf16* E, long lde, hipStream_t s) {
   if (!nt4_ld_ok(lda, ldb, ldc) || (E && !nt4_ld_ok(lda, ldb, lde))) return hipErrorInvalidValue;
   if (!E) return nt4_launch<0>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s);
+  if (b == 128) return nt4_launch<2>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+  if (b != 256) return hipErrorInvalidValue;
   return nt4_launch<1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
 }
 

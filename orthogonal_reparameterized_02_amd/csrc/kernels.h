@@ -66,13 +66,13 @@ bool mfma_nt_ok(int M, int N, int K);
 hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
                           hipStream_t s);
-// C = A B^T as above (one batch) and, per 256-column tile g of C (one
-// orthogonal block of size 256), E[:, g] = C[:, g] Bk[g]^T with Bk [N/256][256][256].
+// C = A B^T as above (one batch) and, per b-column block g of C (b = 256 or
+// 128), E[:, g] = C[:, g] Bk[g]^T with Bk [N/b][b][b].
 // E == nullptr: C only, from the same main loop (bitwise the same C).
 bool mfma_nt_block_ok(int M, int N, int K, int b);
-hipError_t launch_mfma_nt_block(int M, int N, int K, const bf16* A, long lda, const bf16* B,
-                                long ldb, bf16* C, long ldc, const bf16* Bk, bf16* E, long lde,
-                                hipStream_t s);
+hipError_t launch_mfma_nt_block(int M, int N, int K, int b, const bf16* A, long lda,
+                                const bf16* B, long ldb, bf16* C, long ldc, const bf16* Bk,
+                                bf16* E, long lde, hipStream_t s);
 // per-token block products for b in {128, 256}:
 // Out[t][j b + n] = sum_k A[t][j b + k] G[j][n][k]  (A, Out row pitch `width`)
 bool mfma_blocks_ok(int b);
