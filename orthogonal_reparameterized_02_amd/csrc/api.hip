@@ -131,7 +131,8 @@ BwdWs bwd_ws(const poetx_shape* sh, bool xmem = false) {
   if (use_mfma(sh)) {
     const size_t pr = tn_partial_bytes(sh->m / sh->b, sh->b, sh->T);
     const size_t pp = tn_partial_bytes(sh->n / sh->b, sh->b, sh->T);
-    part = align_up(pr > pp ? pr : pp);
+    const size_t pb = tn_partial_bytes(sh->m / sh->b + sh->n / sh->b, sh->b, sh->T);
+    part = align_up(std::max(pb, std::max(pr, pp)));
   }
   w.Z = w.part + part;
   w.total = w.Z + (xmem ? align_up((size_t)sh->T * sh->m * es) : 0);
@@ -287,8 +288,13 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   if ((e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s)) != hipSuccess)
     return dev_fail(e, "R-side blocks (bwd)");
   mark(2, s);
-  // dG_Ri = dS_i^T Z_i
-  if ((e = tn<TS>(mf, m / b, b, T, dS, m, Z, m, dG_R, part, s)) != hipSuccess)
+  // dG_Ri = dS_i^T Z_i.  Where both reductions split the tokens on MFMA
+  // (b >= 256), dG_R waits for dG_P and the two run as one launch: half the
+  // fp32 partials of two launches, and one reduction pass (dS and Z stay
+  // untouched in between).
+  bool dg_joint = false;
+  if constexpr (sizeof(TS) == 2) dg_joint = mf && mfma_tn2_ok(m / b, n / b, b, T);
+  if (!dg_joint && (e = tn<TS>(mf, m / b, b, T, dS, m, Z, m, dG_R, part, s)) != hipSuccess)
     return dev_fail(e, "dG_R");
   mark(3, s);
   {
@@ -314,7 +320,14 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   }
   mark(5, s);
   // dG_Pj = dV_j^T U_j
-  if ((e = tn<TS>(mf, n / b, b, T, dV, n, U, n, dG_P, part, s)) != hipSuccess)
+  if constexpr (sizeof(TS) == 2) {
+    if (dg_joint) {
+      if ((e = launch_mfma_tn2(m / b, n / b, b, T, dS, m, Z, m, dG_R, dV, n, U, n, dG_P, part, s)) !=
+          hipSuccess)
+        return dev_fail(e, "dG_R and dG_P");
+    }
+  }
+  if (!dg_joint && (e = tn<TS>(mf, n / b, b, T, dV, n, U, n, dG_P, part, s)) != hipSuccess)
     return dev_fail(e, "dG_P");
   mark(6, s);
   // dx[:, pi_P[c]] = dU[:, c]  <=>  dx = dU[:, pi_P^{-1}]

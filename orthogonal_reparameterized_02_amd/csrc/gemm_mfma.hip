@@ -559,10 +559,14 @@ __device__ __forceinline__ bf16x8_t frag_tr(const char* p0, const char* p1) {
 // lane holds.  The 16-byte chunk index of a token row is XORed with
 // 2 * (token % 4), so the four rows one read touches fall on distinct banks.
 // Output: an fp32 TILE x TILE partial, staged through LDS for 16-byte stores.
+// One launch can serve two operand pairs of the same D (dG_R and dG_P):
+// batch entries below nb0 read (A0, B0), the rest (A1, B1).
 template <int TILE>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_tn4(
-    int T, int tsplit, int tiles1, const bf16* __restrict__ A, long lda, long sA,
-    const bf16* __restrict__ B, long ldb, long sB, float* __restrict__ P, long ldp, long sP, long sS) {
+    int T, int tsplit, int tiles1, const bf16* __restrict__ A0, long lda0, long sA,
+    const bf16* __restrict__ B0, long ldb0, long sB, float* __restrict__ P, long ldp, long sP,
+    long sS, int nb0, const bf16* __restrict__ A1, long lda1, const bf16* __restrict__ B1,
+    long ldb1) {
   constexpr int WT = TILE / 2, FM = WT / 32, FN = WT / 32, NF = FM + FN;
   constexpr int MPG = FM * FN / NF;               // MFMAs per group
   constexpr int ROWB_T = TILE * 2;                // LDS bytes per token row
@@ -573,10 +577,16 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
   const int tr = blockIdx.x / tiles1, tc = blockIdx.x % tiles1;
-  const long bt = blockIdx.y;
+  // batch entries from nb0 on belong to the second operand pair (A1, B1);
+  // the partials are indexed over both
+  const bool second = (int)blockIdx.y >= nb0;
+  const long bt = second ? (long)blockIdx.y - nb0 : (long)blockIdx.y;
+  const bf16* __restrict__ A = second ? A1 : A0;
+  const bf16* __restrict__ B = second ? B1 : B0;
+  const long lda = second ? lda1 : lda0, ldb = second ? ldb1 : ldb0;
   const int s = blockIdx.z;
   const int t_begin = s * tsplit, t_end = min(T, t_begin + tsplit);
-  P += s * sS + bt * sP;
+  P += s * sS + (long)blockIdx.y * sP;
   const int ntok = max(0, t_end - t_begin);
   const int nk = max(1, (ntok + 31) / 32);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
@@ -899,11 +909,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
 
 // out[e] = sum_{s < S} P[s * stride + e], fixed order
 __global__ void k_reduce_splits(long n, int S, long stride, const float* __restrict__ P,
-                                float* __restrict__ out) {
+                                float* __restrict__ out, long n0, float* __restrict__ out1) {
   for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
     float acc = P[e];
     for (int s = 1; s < S; ++s) acc += P[s * stride + e];
-    out[e] = acc;
+    if (e < n0) out[e] = acc;
+    else out1[e - n0] = acc;
   }
 }
 
@@ -1046,6 +1057,38 @@ size_t tn_partial_bytes(int batch, int D, int T) {
   return S > 1 ? (size_t)S * batch * D * D * sizeof(float) : 0;
 }
 
+namespace {
+
+// k_tn4 over `batch` D x D products (D a multiple of 256) in S token splits;
+// entries from nb0 on read (A1, B1).  Writes P[s][batch][D][D].
+hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, long lda0,
+                      const bf16* B0, long ldb0, const bf16* A1, long lda1, const bf16* B1,
+                      long ldb1, float* P, hipStream_t s) {
+  constexpr int lds = 4 * 2 * 32 * 256 * 2;  // four stages of 32 tokens x (A, B) rows
+  static const hipError_t attr = set_lds(k_tn4<256>, lds);
+  if (attr != hipSuccess) return attr;
+  const long dd = (long)D * D;
+  const int tiles1 = D / 256;
+  const int tsplit = ((T + S - 1) / S + 31) / 32 * 32;
+  // a split's buffer range (tsplit rows of the widest operand) stays below 2^31 bytes
+  if ((long)tsplit * std::max(std::max(lda0, ldb0), std::max(lda1, ldb1)) * 2 >= (1L << 31))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_tn4<256>, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit,
+                     tiles1, A0, lda0, (long)D, B0, ldb0, (long)D, P, (long)D, dd, dd * batch, nb0,
+                     A1, lda1, B1, ldb1);
+  return hipGetLastError();
+}
+
+// out0 = the first n0 sums over S partials of stride n, out1 = the rest
+hipError_t reduce_launch(long n, int S, const float* P, float* out0, long n0, float* out1,
+                         hipStream_t s) {
+  const int grid = (int)std::min<long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(k_reduce_splits, dim3(grid), dim3(256), 0, s, n, S, n, P, out0, n0, out1);
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long sA, const bf16* B,
                           long ldb, long sB, float* out, float* partials, hipStream_t s) {
   const int S = tn_splits(batch, D, T);
@@ -1053,24 +1096,32 @@ hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long
   float* P = S > 1 ? partials : out;
   hipError_t e;
   if (D >= 256) {
-    constexpr int lds = 4 * 2 * 32 * 256 * 2;  // four stages of 32 tokens x (A, B) rows
-    static const hipError_t attr = set_lds(k_tn4<256>, lds);
-    if (attr != hipSuccess) return attr;
-    const int tiles1 = D / 256;
-    const int tsplit = ((T + S - 1) / S + 31) / 32 * 32;
-    hipLaunchKernelGGL(k_tn4<256>, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit,
-                       tiles1, A, lda, sA, B, ldb, sB, P, (long)D, dd, dd * batch);
-    e = hipGetLastError();
+    if (sA != D || sB != D) return hipErrorInvalidValue;
+    e = tn4_launch(batch, batch, D, T, S, A, lda, B, ldb, A, lda, B, ldb, P, s);
   } else if (D == 64) {
     e = tn_launch<64>(batch, D, T, S, A, lda, sA, B, ldb, sB, P, D, dd, dd * batch, s);
   } else {
     e = tn_launch<128>(batch, D, T, S, A, lda, sA, B, ldb, sB, P, D, dd, dd * batch, s);
   }
   if (e != hipSuccess || S == 1) return e;
-  const long n = dd * batch;
-  const int grid = (int)std::min<long>((n + 255) / 256, 4096);
-  hipLaunchKernelGGL(k_reduce_splits, dim3(grid), dim3(256), 0, s, n, S, n, P, out);
-  return hipGetLastError();
+  return reduce_launch(dd * batch, S, P, out, dd * batch, nullptr, s);
+}
+
+bool mfma_tn2_ok(int nb0, int nb1, int D, int T) {
+  return D >= 256 && D % 256 == 0 && tn_splits(nb0 + nb1, D, T) > 1;
+}
+
+hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long lda0,
+                           const bf16* B0, long ldb0, float* out0, const bf16* A1, long lda1,
+                           const bf16* B1, long ldb1, float* out1, float* partials,
+                           hipStream_t s) {
+  if (!mfma_tn2_ok(nb0, nb1, D, T)) return hipErrorInvalidValue;
+  const int batch = nb0 + nb1;
+  const int S = tn_splits(batch, D, T);
+  const long dd = (long)D * D;
+  hipError_t e = tn4_launch(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, partials, s);
+  if (e != hipSuccess) return e;
+  return reduce_launch(dd * batch, S, partials, out0, dd * nb0, out1, s);
 }
 
 }  // namespace poetx
