@@ -51,13 +51,25 @@ __device__ __forceinline__ void tile_pair(int p, int nt, int& I, int& J) {
   J = I + p;
 }
 
+// Offset of Q[i][j] in a b x b block of Qg.  Blocks that fit LDS (b <= 256)
+// are row-major.  Larger ones are read only as the MFMA A operand, straight
+// from L2, so they are stored in operand-fragment order: for row tile i/32
+// and K-step j/16, the 32 x 16 fragment is 1 KB laid out as the 64 lanes'
+// 16-byte pieces (lane i%32 + 32*((j%16)/8) holds j%16 = 8h .. 8h+7).  One
+// wave's fragment load is then 8 whole cache lines instead of 32 partial
+// ones.
+__device__ __forceinline__ long q_off(int i, int j, int b, bool frag) {
+  if (!frag) return (long)i * b + j;
+  return ((long)((i >> 5) * (b >> 4) + (j >> 4)) * 64 + (i & 31) + 32 * ((j >> 3) & 1)) * 8 + (j & 7);
+}
+
 // Qg[blk] = Q as bf16.  One workgroup per tile pair (I, J): the packed
 // parameters of tile (I, J) (row segments, contiguous in theta) go to LDS;
 // tile (I, J) of Q is written from it and tile (J, I) = -(tile)^T from the
 // transposed LDS reads, both with 16-byte row stores.  Diagonal tiles hold
 // both halves and the zero diagonal.
 __global__ __launch_bounds__(256) void k_unpack_q(int b, const float* __restrict__ theta,
-                                                  bf16* __restrict__ Qg) {
+                                                  bf16* __restrict__ Qg, int frag) {
   __shared__ float tile[TT][TT + 1];
   const int blk = blockIdx.y, nt = b / TT;
   const int tb = b * (b - 1) / 2;
@@ -95,13 +107,13 @@ __global__ __launch_bounds__(256) void k_unpack_q(int b, const float* __restrict
     v.y = pack2bf(up[2], up[3]);
     v.z = pack2bf(up[4], up[5]);
     v.w = pack2bf(up[6], up[7]);
-    *reinterpret_cast<uint4*>(q + (long)i * b + J * TT + c0) = v;
+    *reinterpret_cast<uint4*>(q + q_off(i, J * TT + c0, b, frag)) = v;
     if (I != J) {
       v.x = pack2bf(lo[0], lo[1]);
       v.y = pack2bf(lo[2], lo[3]);
       v.z = pack2bf(lo[4], lo[5]);
       v.w = pack2bf(lo[6], lo[7]);
-      *reinterpret_cast<uint4*>(q + (long)(J * TT + r) * b + I * TT + c0) = v;
+      *reinterpret_cast<uint4*>(q + q_off(J * TT + r, I * TT + c0, b, frag)) = v;
     }
   }
 }
@@ -140,14 +152,18 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   bf16* Xs = reinterpret_cast<bf16*>(smem);         // [PW][QP]: X^T
   bf16* Qs = Xs + PW * QP;                          // [B][QP] (QLDS only)
 
-  // Workgroups are dealt round-robin over the 8 XCDs; renumber them so the
-  // panels of one block share an XCD, and so its L2 copy of Q (read by every
-  // panel) is fetched from MALL/HBM once instead of once per XCD.
+  // Workgroups are dealt round-robin over the 8 XCDs; renumber them so each
+  // XCD walks a contiguous range of (block, panel) pairs.  The panels of one
+  // block then share an XCD (a block may straddle two), its L2 copy of Q
+  // (read by every panel) is fetched from MALL/HBM once instead of once per
+  // XCD, and an XCD's L2 holds the Q of only the few blocks it has in flight.
   int pan = blockIdx.x, blk = blockIdx.y;
-  if (gridDim.y % 8 == 0) {
-    const int id = blockIdx.y * gridDim.x + blockIdx.x, xcd = id % 8, slot = id / 8;
-    blk = xcd * (gridDim.y / 8) + slot / gridDim.x;
-    pan = slot % gridDim.x;
+  const int nwg = gridDim.x * gridDim.y;
+  if (nwg % 8 == 0) {
+    const int id = blockIdx.y * gridDim.x + blockIdx.x;
+    const int pid = (id % 8) * (nwg / 8) + id / 8;
+    blk = pid / gridDim.x;
+    pan = pid % gridDim.x;
   }
   const int J0 = pan * PW;
   const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
@@ -278,9 +294,50 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     f32x16_t P[RTW];
 #pragma unroll
     for (int t = 0; t < RTW; ++t) P[t] = (f32x16_t){};
-    if (wave < RT) {  // waves beyond the block's row tiles only join the barriers
-      // operand fragments double-buffered: the reads for k0+16 are issued
-      // before the MFMAs of k0
+    if (!QLDS && wave < RT) {
+      // Q streamed from L2: its fragments run QPF K-steps ahead of the
+      // MFMAs (an L2 round trip is several K-steps of MFMA work); the X
+      // fragments come from LDS one K-step ahead.  Fully unrolled, so every
+      // ring index is a constant.
+      constexpr int QPF = MODE == MODE_BWD2 ? 4 : 8;
+      constexpr int NKS = B / 16;
+      uint4 bq[2], aq[QPF][RTW];
+      // one row offset per row tile; the K offset (ks * 32 bytes < 1 KB)
+      // becomes the load's immediate offset.  Q is the same in every step,
+      // so the offsets pass through an empty asm each step: otherwise the
+      // compiler hoists all of the wave's Q loads out of the step loop and
+      // tries to keep its 64 KB of Q in registers.  (An offset, not the
+      // pointer: a pointer through asm loses its global address space and
+      // the loads become flat ones, which also count against lgkmcnt.)
+      int qoff[RTW];
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) {
+        qoff[t] = (int)q_off(min(wave + t * NWAVE, RT - 1) * 32 + (lane % 32), 8 * (lane / 32), B, true);
+        asm volatile("" : "+v"(qoff[t]));
+      }
+      const bf16* xrow = Xs + col * QP + 8 * (lane / 32);
+      auto fetch_a = [&](int ks, int s) {  // fragment order: K-step ks is 1 KB further
+#pragma unroll
+        for (int t = 0; t < RTW; ++t)
+          aq[s][t] = *reinterpret_cast<const uint4*>(Qb + qoff[t] + ks * 512);
+      };
+      auto fetch_b = [&](int ks, int s) { bq[s] = *reinterpret_cast<const uint4*>(xrow + ks * 16); };
+#pragma unroll
+      for (int i = 0; i < QPF; ++i) fetch_a(i, i);
+      fetch_b(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) fetch_b(ks + 1, (ks + 1) & 1);
+#pragma unroll
+        for (int t = 0; t < RTW; ++t)
+          if (RTW * NWAVE == RT || wave + t * NWAVE < RT)
+            P[t] = mfma32x32x16(as_bf16x8(aq[ks % QPF][t]), as_bf16x8(bq[ks & 1]), P[t]);
+        if (ks + QPF < NKS) fetch_a(ks + QPF, ks % QPF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (QLDS && wave < RT) {  // waves beyond the block's row tiles only join the barriers
+      // Q in LDS: operand fragments double-buffered, the reads for k0+16
+      // issued before the MFMAs of k0
       uint4 bq[2], aq[2][RTW];
       auto fetch = [&](int k0, int s) {
         const int kk = k0 + 8 * (lane / 32);
@@ -288,8 +345,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
         for (int t = 0; t < RTW; ++t) {
           const int arow = min(wave + t * NWAVE, RT - 1) * 32 + (lane % 32);
-          if constexpr (QLDS) aq[s][t] = *reinterpret_cast<const uint4*>(Qs + arow * QP + kk);
-          else aq[s][t] = *reinterpret_cast<const uint4*>(Qb + (long)arow * B + kk);
+          aq[s][t] = *reinterpret_cast<const uint4*>(Qs + arow * QP + kk);
         }
       };
       auto mma = [&](int s) {
@@ -447,7 +503,9 @@ hipError_t dispatch_panel(int nblk, int b, int k, const float* theta, const bf16
 // LDS, larger ones stream it through L2 as the MFMA A operand
 hipError_t unpack(int nblk, int b, const float* theta, bf16* Qg, hipStream_t s) {
   const int nt = b / TT;
-  hipLaunchKernelGGL(k_unpack_q, dim3(nt * (nt + 1) / 2, nblk), dim3(256), 0, s, b, theta, Qg);
+  const int frag = b > 256;  // the panel kernel streams these blocks' Q from L2
+  hipLaunchKernelGGL(k_unpack_q, dim3(nt * (nt + 1) / 2, nblk), dim3(256), 0, s, b, theta, Qg,
+                     frag);
   return hipGetLastError();
 }
 

@@ -271,10 +271,12 @@ def test_xmem_bitwise_equals_xfast(name, T):
         np.testing.assert_array_equal(a, b)
 
 
-def test_xmem_parity_small_T():
-    """The memory-saving mode against the oracle directly."""
+@pytest.mark.parametrize("T", [72, 600])
+def test_xmem_parity_small_T(T):
+    """The memory-saving mode against the oracle directly (T = 600: the
+    joint dG reduction over three token splits, the last one ragged)."""
     cfg = I.CONFIG_BY_NAME["square"]
-    T = 72
+    say(f"xmem parity square T={T}")
     d = I.make_inputs(cfg, seed=23, T=T)
     L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype), xmem=True)
     L.load(to_dev(d["W0"]), to_dev(d["theta_P"]), to_dev(d["theta_R"]),
