@@ -171,7 +171,6 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   const long boff = (long)blk * B * B;
   const bf16* Qb = Qg + boff;
   const float* Db = D ? D + boff : nullptr;
-  const float* th = theta + (long)blk * (B * (B - 1) / 2);
 
   // Prologue: every global load (Q, and for phase 1 the band D[J0..J0+31][:])
   // goes out before the first LDS write.
@@ -242,6 +241,24 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     }
     if constexpr (MODE == MODE_FWD) __syncthreads();  // Q visible for the base
   }
+  if constexpr (MODE == MODE_FWD && !QLDS) {
+    // Q[row][J0+col] = -Q[J0+col][row]: rows J0.. of Q are one row tile in
+    // fragment order, and a lane's four accumulator rows 8a + 4h .. +3 of
+    // row tile rt are four consecutive elements of one 16-byte piece
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int rt = min(wave + t * NWAVE, RT - 1);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const uint2 v = *reinterpret_cast<const uint2*>(
+            Qb + q_off(J0 + col, rt * 32 + 8 * a + 4 * (lane / 32), B, true));
+        base[t][4 * a + 0] = -bf2f((bf16)(v.x & 0xffff));
+        base[t][4 * a + 1] = -bf2f((bf16)(v.x >> 16));
+        base[t][4 * a + 2] = -bf2f((bf16)(v.y & 0xffff));
+        base[t][4 * a + 3] = -bf2f((bf16)(v.y >> 16));
+      }
+    }
+  }
   f32x16_t X[RTW];
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
@@ -252,7 +269,6 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
         const int row = rt * 32 + acc_row(r, lane);
         if constexpr (MODE == MODE_FWD) {
           if constexpr (QLDS) base[t][r] = bf2f(Qs[row * QP + J0 + col]);
-          else base[t][r] = skew_at_nb(th, row, J0 + col, B);
         } else if constexpr (MODE == MODE_BWD2) {
           base[t][r] = Db[(long)row * B + J0 + col];
         }
@@ -295,11 +311,12 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 #pragma unroll
     for (int t = 0; t < RTW; ++t) P[t] = (f32x16_t){};
     if (!QLDS && wave < RT) {
-      // Q streamed from L2: its fragments run QPF K-steps ahead of the
-      // MFMAs (an L2 round trip is several K-steps of MFMA work); the X
-      // fragments come from LDS one K-step ahead.  Fully unrolled, so every
-      // ring index is a constant.
-      constexpr int QPF = MODE == MODE_BWD2 ? 4 : 8;
+      // Q streamed from L2 in fragment order: each fragment load is 1 KB of
+      // whole lines, issued QPF K-steps ahead of its MFMAs (deeper rings
+      // measured no faster: the loop is bound by the CU's L2 bandwidth, 512
+      // KB of Q per step for eight waves); the X fragments come from LDS one
+      // K-step ahead.  Fully unrolled, so every ring index is a constant.
+      constexpr int QPF = 2;
       constexpr int NKS = B / 16;
       uint4 bq[2], aq[QPF][RTW];
       // one row offset per row tile; the K offset (ks * 32 bytes < 1 KB)

@@ -58,13 +58,6 @@ __device__ __forceinline__ float skew_at(const float* th, int i, int j, int b) {
   return 0.0f;
 }
 
-// Q[i][j] without divergent branches: always one load, then select
-__device__ __forceinline__ float skew_at_nb(const float* th, int i, int j, int b) {
-  const int lo = min(i, j), hi = max(i, j);
-  const float v = th[lo == hi ? 0 : tri_index(lo, hi, b)];
-  return i < j ? v : (i > j ? -v : 0.0f);
-}
-
 // (i, j), i < j, of packed index t: row i holds t in [S(i), S(i+1)) with
 // S(i) = i*b - i*(i+1)/2
 __device__ __forceinline__ void tri_rc(int t, int b, int& i, int& j) {
