@@ -63,6 +63,8 @@ CNP_CASES = [  # nblk, b, k, dtype, sigma
     (5, 256, 2, "bf16", 0.01),
     (3, 512, 5, "bf16", 0.005),
     (37, 512, 5, "bf16", 0.005),
+    (2, 512, 0, "bf16", 0.005),
+    (2, 512, 1, "bf16", 0.005),
 ]
 
 
