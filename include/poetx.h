@@ -122,6 +122,24 @@ int32_t poetx_cnp_bwd(int32_t nblk, int32_t b, int32_t k, const float* theta,
                       int32_t prec, void* ws, size_t ws_bytes,
                       poetx_stream_t stream);
 
+/*
+ * poetx_cnp_bwd_after_fwd -- poetx_cnp_bwd for the step's own forward pass:
+ * the same arguments and results (bitwise), but `ws` must be the workspace
+ * that last served poetx_cnp_fwd with the same nblk, b, k, theta and
+ * precision (g_dtype = prec), untouched since.  On the bf16 MFMA path the
+ * forward leaves the unpacked Q at the start of its workspace and this call
+ * reads it there instead of unpacking theta again (one kernel less); other
+ * configurations do exactly what poetx_cnp_bwd does.  ws is sized for the
+ * backward, poetx_cnp_workspace_bytes(nblk, b, k, 1, prec), which also
+ * serves the forward.  Passing a workspace that does not hold that Q gives
+ * wrong dtheta; it is not detected.
+ * Errors as poetx_cnp_bwd.
+ */
+int32_t poetx_cnp_bwd_after_fwd(int32_t nblk, int32_t b, int32_t k, const float* theta,
+                                const float* dG, float* dtheta, int32_t accumulate,
+                                int32_t prec, void* ws, size_t ws_bytes,
+                                poetx_stream_t stream);
+
 /* Workspace bytes for poetx_cnp_fwd (which = 0) or poetx_cnp_bwd (1) with
  * float32 (act = POETX_F32) or bf16 (POETX_BF16) activations;
  * 0 on bad arguments. */

@@ -23,6 +23,7 @@ SIGNATURES = {
     "poetx_last_error": (C.c_char_p, []),
     "poetx_cnp_fwd": (_i, [_i, _i, _i, _p, _p, _p, _i, _p, _sz, _p]),
     "poetx_cnp_bwd": (_i, [_i, _i, _i, _p, _p, _p, _i, _i, _p, _sz, _p]),
+    "poetx_cnp_bwd_after_fwd": (_i, [_i, _i, _i, _p, _p, _p, _i, _i, _p, _sz, _p]),
     "poetx_cnp_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "poetx_fold_perm": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "poetx_layer_fwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),

@@ -362,6 +362,36 @@ int32_t merge_impl(const poetx_shape* sh, const TS* W0f, const TS* G_R, const TS
   return ok();
 }
 
+// the CNP backward; q_ready: ws already holds the forward's unpacked Q
+int32_t cnp_bwd_impl(const char* fn, int32_t nblk, int32_t b, int32_t k, const float* theta,
+                     const float* dG, float* dtheta, int32_t accumulate, int32_t prec, void* ws,
+                     size_t ws_bytes, poetx_stream_t stream, bool q_ready) {
+  const int32_t act = prec;
+  int32_t st = check_cnp_args(fn, nblk, b, k, act);
+  if (st != POETX_OK) return st;
+  NEED_PTR(theta);
+  NEED_PTR(dG);
+  NEED_PTR(dtheta);
+  const size_t need = cnp_ws(nblk, b, k, 1, act);
+  if (need) {
+    NEED_PTR(ws);
+    if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  }
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (cnp_uses_panel(b, act)) {
+    const size_t bb = (size_t)b * b;
+    bf16* Qg = (bf16*)ws;  // the forward's workspace holds the same Q at the same place
+    bf16* F = at<bf16>(ws, align_up(nblk * bb * 2));
+    float* dQ = at<float>(ws, align_up(nblk * bb * 2) + align_up((size_t)k * nblk * bb * 2));
+    e = launch_cnp_panel_bwd(nblk, b, k, theta, dG, dtheta, accumulate, Qg, F, dQ, q_ready, s);
+  } else {
+    e = launch_cnp_small_bwd(nblk, b, k, theta, dG, dtheta, accumulate, (float*)ws, s);
+  }
+  if (e != hipSuccess) return dev_fail(e, fn);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -412,34 +442,19 @@ int32_t poetx_cnp_fwd(int32_t nblk, int32_t b, int32_t k, const float* theta, vo
   return ok();
 }
 
+
 int32_t poetx_cnp_bwd(int32_t nblk, int32_t b, int32_t k, const float* theta, const float* dG,
                       float* dtheta, int32_t accumulate, int32_t prec, void* ws,
                       size_t ws_bytes, poetx_stream_t stream) {
-  const char* fn = "poetx_cnp_bwd";
-  const int32_t act = prec;
-  int32_t st = check_cnp_args(fn, nblk, b, k, act);
-  if (st != POETX_OK) return st;
-  NEED_PTR(theta);
-  NEED_PTR(dG);
-  NEED_PTR(dtheta);
-  const size_t need = cnp_ws(nblk, b, k, 1, act);
-  if (need) {
-    NEED_PTR(ws);
-    if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
-  }
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (cnp_uses_panel(b, act)) {
-    const size_t bb = (size_t)b * b;
-    bf16* Qg = (bf16*)ws;
-    bf16* F = at<bf16>(ws, align_up(nblk * bb * 2));
-    float* dQ = at<float>(ws, align_up(nblk * bb * 2) + align_up((size_t)k * nblk * bb * 2));
-    e = launch_cnp_panel_bwd(nblk, b, k, theta, dG, dtheta, accumulate, Qg, F, dQ, s);
-  } else {
-    e = launch_cnp_small_bwd(nblk, b, k, theta, dG, dtheta, accumulate, (float*)ws, s);
-  }
-  if (e != hipSuccess) return dev_fail(e, fn);
-  return ok();
+  return cnp_bwd_impl("poetx_cnp_bwd", nblk, b, k, theta, dG, dtheta, accumulate, prec, ws,
+                      ws_bytes, stream, false);
+}
+
+int32_t poetx_cnp_bwd_after_fwd(int32_t nblk, int32_t b, int32_t k, const float* theta,
+                                const float* dG, float* dtheta, int32_t accumulate, int32_t prec,
+                                void* ws, size_t ws_bytes, poetx_stream_t stream) {
+  return cnp_bwd_impl("poetx_cnp_bwd_after_fwd", nblk, b, k, theta, dG, dtheta, accumulate, prec,
+                      ws, ws_bytes, stream, true);
 }
 
 int32_t poetx_fold_perm(int32_t m, int32_t n, int32_t dt, const void* W0, const int32_t* perm_R,

@@ -537,8 +537,8 @@ hipError_t launch_cnp_panel_fwd(int nblk, int b, int k, const float* theta, bf16
 
 hipError_t launch_cnp_panel_bwd(int nblk, int b, int k, const float* theta, const float* dG,
                                 float* dtheta, int accumulate, bf16* ws_Q, bf16* ws_F,
-                                float* ws_dQ, hipStream_t s) {
-  hipError_t e = unpack(nblk, b, theta, ws_Q, s);
+                                float* ws_dQ, bool q_ready, hipStream_t s) {
+  hipError_t e = q_ready ? hipSuccess : unpack(nblk, b, theta, ws_Q, s);
   if (e != hipSuccess) return e;
   if (k > 0) {
     e = dispatch_panel<MODE_BWD1>(nblk, b, k, theta, ws_Q, dG, ws_F, nullptr, nullptr, s);

@@ -99,9 +99,10 @@ hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long 
 // ws_Q: nblk*b*b bf16 scratch holding the unpacked skew blocks.
 hipError_t launch_cnp_panel_fwd(int nblk, int b, int k, const float* theta, bf16* G,
                                 bf16* GT, bf16* ws_Q, hipStream_t s);
-// ws_Q as above; ws_F: k*nblk*b*b bf16; ws_dQ: nblk*b*b float.
+// ws_Q as above; ws_F: k*nblk*b*b bf16; ws_dQ: nblk*b*b float.  q_ready:
+// ws_Q already holds the unpacked Q of theta (left by launch_cnp_panel_fwd).
 hipError_t launch_cnp_panel_bwd(int nblk, int b, int k, const float* theta, const float* dG,
                                 float* dtheta, int accumulate, bf16* ws_Q, bf16* ws_F,
-                                float* ws_dQ, hipStream_t s);
+                                float* ws_dQ, bool q_ready, hipStream_t s);
 
 }  // namespace poetx

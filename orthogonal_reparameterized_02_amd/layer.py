@@ -72,8 +72,10 @@ class POETXLayer:
             self.saved = _bytes(P.poetx_saved_bytes(self.sh), dev)
             self.ws_fwd = _bytes(P.poetx_workspace_bytes(self.sh, 0), dev)
             self.ws_bwd = _bytes(P.poetx_workspace_bytes(self.sh, 1), dev)
-        self.ws_cnp_fwd = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 0, act), dev)
-        self.ws_cnp_bwd = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 1, act), dev)
+        # one CNP workspace for both calls (the backward's size covers the
+        # forward's): the backward then reuses the Q the forward unpacked
+        self.ws_cnp = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 1, act), dev)
+        self._q_ready = False
 
     # -- set-up, once per inner loop (untimed) --------------------------------
     def load(self, W0: torch.Tensor, theta_P: torch.Tensor, theta_R: torch.Tensor,
@@ -109,16 +111,19 @@ class POETXLayer:
     def set_theta(self, theta_P: torch.Tensor, theta_R: torch.Tensor) -> None:
         self.theta_P.copy_(theta_P)
         self.theta_R.copy_(theta_R)
+        self._q_ready = False
 
     # -- the hot path ---------------------------------------------------------
     def cnp(self) -> None:
         """G, G^T of every block of both sides, in one call."""
-        P.poetx_cnp_fwd(self.theta, self.b, self.k, self.G, self.GT, self.ws_cnp_fwd)
+        P.poetx_cnp_fwd(self.theta, self.b, self.k, self.G, self.GT, self.ws_cnp)
+        self._q_ready = True
 
     def cnp_bwd(self) -> None:
-        """dtheta of both sides from dG, in one call."""
+        """dtheta of both sides from dG, in one call (reusing the forward's
+        unpacked Q when theta has not changed since cnp())."""
         P.poetx_cnp_bwd(self.theta, self.dG, self.b, self.k, self.dtheta, self.act,
-                        ws=self.ws_cnp_bwd)
+                        ws=self.ws_cnp, after_fwd=self._q_ready)
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
         self.cnp()

@@ -91,12 +91,15 @@ def poetx_cnp_fwd(theta: torch.Tensor, b: int, k: int, G: torch.Tensor,
 
 def poetx_cnp_bwd(theta: torch.Tensor, dG: torch.Tensor, b: int, k: int, dtheta: torch.Tensor,
                   prec: int, accumulate: bool = False, ws: Optional[torch.Tensor] = None,
-                  stream=None) -> None:
+                  stream=None, after_fwd: bool = False) -> None:
+    """after_fwd: call poetx_cnp_bwd_after_fwd (ws last served poetx_cnp_fwd
+    with this theta and still holds its unpacked Q)."""
     nblk = theta.shape[0]
     tb = b * (b - 1) // 2
     need = poetx_cnp_workspace_bytes(nblk, b, k, 1, prec)
     wp, wb = _ws(ws, need)
-    check("poetx_cnp_bwd", lib().poetx_cnp_bwd(
+    name = "poetx_cnp_bwd_after_fwd" if after_fwd else "poetx_cnp_bwd"
+    check(name, getattr(lib(), name)(
         nblk, b, k, _dev(theta, "theta", torch.float32, nblk * tb),
         _dev(dG, "dG", torch.float32, nblk * b * b), _dev(dtheta, "dtheta", torch.float32, nblk * tb),
         int(bool(accumulate)), prec, wp, wb, _stream(stream)))

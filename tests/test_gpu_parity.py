@@ -114,6 +114,32 @@ def test_cnp_bwd(nblk, b, k, dtype, sigma, accumulate):
     assert err <= TOL[dtype]
 
 
+@pytest.mark.parametrize("accumulate", [False, True])
+@pytest.mark.parametrize("nblk,b,k,dtype,sigma", [(32, 256, 4, "bf16", 0.01), (16, 128, 4, "bf16", 0.01),
+                                                  (3, 512, 5, "bf16", 0.005), (5, 64, 3, "f32", 0.02)])
+def test_cnp_bwd_after_fwd_bitwise(nblk, b, k, dtype, sigma, accumulate):
+    """The backward that reuses the forward's unpacked Q (the workspace
+    that served poetx_cnp_fwd) gives poetx_cnp_bwd's dtheta bit for bit."""
+    say(f"cnp_bwd_after_fwd nblk={nblk} b={b} k={k} {dtype} acc={accumulate}")
+    th, dG = _cnp_inputs(nblk, b, sigma, 2000 + b + k)
+    tb = b * (b - 1) // 2
+    prior = np.random.default_rng(6).standard_normal((nblk, tb)).astype(np.float32)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    G = torch.empty(nblk, b, b, dtype=tdt, device="cuda")
+    ws = torch.empty(max(16, P.poetx_cnp_workspace_bytes(nblk, b, k, 1, act_of(dtype))),
+                     dtype=torch.uint8, device="cuda")
+    th_d, dG_d = to_dev(th), to_dev(dG)
+    outs = []
+    for after in (False, True):
+        ws.fill_(0x5A)  # the reuse must not depend on anything but the forward's writes
+        P.poetx_cnp_fwd(th_d, b, k, G, None, ws)
+        dth = to_dev(prior.copy())
+        P.poetx_cnp_bwd(th_d, dG_d, b, k, dth, act_of(dtype), accumulate, ws, after_fwd=after)
+        torch.cuda.synchronize()
+        outs.append(bits(dth).copy())
+    np.testing.assert_array_equal(outs[0], outs[1])
+
+
 # ------------------------------------------------------------------ the layer
 def run_layer(cfg, d, T):
     L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype))
