@@ -119,9 +119,9 @@ __global__ __launch_bounds__(NTHR) void k_permute_rows_v(int rows, int width,
           t[4 * h + 2] = row[ix[u][h].z];
           t[4 * h + 3] = row[ix[u][h].w];
         }
-        uint4 pk;
+        u32x4 pk;
         __builtin_memcpy(&pk, t, 16);
-        reinterpret_cast<uint4*>(out + (long)(r0 + rr) * width)[v] = pk;
+        __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(out + (long)(r0 + rr) * width) + v);
       }
     }
   }
