@@ -96,7 +96,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # The step has a fixed shape and fixed buffers, so it is captured once as
-    # a HIP graph (21 kernels, no memsets) and replayed: the same kernels on
+    # a HIP graph (15 kernels, no memsets) and replayed: the same kernels on
     # the same data, without a host launch per kernel.  --eager launches them.
     if args.eager:
         run_step = lambda: L.step(x, dy)  # noqa: E731
