@@ -288,9 +288,9 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   if ((e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s)) != hipSuccess)
     return dev_fail(e, "R-side blocks (bwd)");
   mark(2, s);
-  // dG_Ri = dS_i^T Z_i.  Where both reductions split the tokens on MFMA
-  // (b >= 256), dG_R waits for dG_P and the two run as one launch: half the
-  // fp32 partials of two launches, and one reduction pass (dS and Z stay
+  // dG_Ri = dS_i^T Z_i.  Where both reductions split the tokens on MFMA,
+  // dG_R waits for dG_P and the two run as one launch: half the fp32
+  // partials of two launches, and one reduction pass (dS and Z stay
   // untouched in between).
   bool dg_joint = false;
   if constexpr (sizeof(TS) == 2) dg_joint = mf && mfma_tn2_ok(m / b, n / b, b, T);

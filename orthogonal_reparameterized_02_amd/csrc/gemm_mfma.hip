@@ -703,22 +703,28 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 
 // Partial token reduction: P[s][bt][r][c] = sum_{t in split s} A[t][r] B[t][c]
 // (A, B token-major, column offsets folded into the pointers per batch).
+// Batch entries from nb0 on read the second operand pair (A1, B1), as in
+// k_tn4; the partials are indexed over both.
 template <int BT>
 __global__ __launch_bounds__(256, 1) void k_gemm_tn(int T, int tsplit, int tiles1,
-                                                    const bf16* __restrict__ A, long lda, long sA,
-                                                    const bf16* __restrict__ B, long ldb, long sB,
+                                                    const bf16* __restrict__ A0, long lda0, long sA,
+                                                    const bf16* __restrict__ B0, long ldb0, long sB,
                                                     float* __restrict__ P, long ldp, long sP,
-                                                    long sS) {
+                                                    long sS, int nb0, const bf16* __restrict__ A1,
+                                                    long lda1, const bf16* __restrict__ B1,
+                                                    long ldb1) {
   using C = Cfg<BT, BT, 2, 2>;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
   const int tm = blockIdx.x / tiles1, tn = blockIdx.x % tiles1;
-  const long bt = blockIdx.y;
+  const bool second = (int)blockIdx.y >= nb0;
+  const long bt = second ? (long)blockIdx.y - nb0 : (long)blockIdx.y;
+  const long lda = second ? lda1 : lda0, ldb = second ? ldb1 : ldb0;
   const int s = blockIdx.z;
-  A += bt * sA + tm * BT;
-  B += bt * sB + tn * BT;
-  P += s * sS + bt * sP;
+  const bf16* __restrict__ A = (second ? A1 : A0) + bt * sA + tm * BT;
+  const bf16* __restrict__ B = (second ? B1 : B0) + bt * sB + tn * BT;
+  P += s * sS + (long)blockIdx.y * sP;
   const int t_begin = s * tsplit, t_end = min(T, t_begin + tsplit);
 
   // loader: a wave covers 8 tokens x 8 16-byte feature chunks; the LDS write
@@ -941,16 +947,22 @@ hipError_t nt_launch(int batch, int M, int N, int K, const bf16* A, long lda, lo
 
 template <int BT>
 hipError_t tn_launch(int batch, int D, int T, int S, const bf16* A, long lda, long sA, const bf16* B,
-                     long ldb, long sB, float* P, long ldp, long sP, long sS, hipStream_t s) {
+                     long ldb, long sB, float* P, long ldp, long sP, long sS, hipStream_t s,
+                     int nb0 = -1, const bf16* A1 = nullptr, long lda1 = 0,
+                     const bf16* B1 = nullptr, long ldb1 = 0) {
   using CF = Cfg<BT, BT, 2, 2>;
   auto kern = k_gemm_tn<BT>;
   static const hipError_t attr = set_lds(kern, CF::LDS);
   if (attr != hipSuccess) return attr;
+  if (nb0 < 0) {  // one operand pair
+    nb0 = batch;
+    A1 = A, lda1 = lda, B1 = B, ldb1 = ldb;
+  }
   const int tiles1 = D / BT;
   const int tsplit = ((T + S - 1) / S + BK - 1) / BK * BK;
   constexpr int lds = CF::LDS;
   hipLaunchKernelGGL(kern, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit, tiles1,
-                     A, lda, sA, B, ldb, sB, P, ldp, sP, sS);
+                     A, lda, sA, B, ldb, sB, P, ldp, sP, sS, nb0, A1, lda1, B1, ldb1);
   return hipGetLastError();
 }
 
@@ -1108,7 +1120,7 @@ hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long
 }
 
 bool mfma_tn2_ok(int nb0, int nb1, int D, int T) {
-  return D >= 256 && D % 256 == 0 && tn_splits(nb0 + nb1, D, T) > 1;
+  return (D == 64 || D == 128 || D % 256 == 0) && tn_splits(nb0 + nb1, D, T) > 1;
 }
 
 hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long lda0,
@@ -1119,7 +1131,15 @@ hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long 
   const int batch = nb0 + nb1;
   const int S = tn_splits(batch, D, T);
   const long dd = (long)D * D;
-  hipError_t e = tn4_launch(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, partials, s);
+  hipError_t e;
+  if (D >= 256)
+    e = tn4_launch(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, partials, s);
+  else if (D == 64)
+    e = tn_launch<64>(batch, D, T, S, A0, lda0, D, B0, ldb0, D, partials, D, dd, dd * batch, s, nb0,
+                      A1, lda1, B1, ldb1);
+  else
+    e = tn_launch<128>(batch, D, T, S, A0, lda0, D, B0, ldb0, D, partials, D, dd, dd * batch, s,
+                       nb0, A1, lda1, B1, ldb1);
   if (e != hipSuccess) return e;
   return reduce_launch(dd * batch, S, partials, out0, dd * nb0, out1, s);
 }

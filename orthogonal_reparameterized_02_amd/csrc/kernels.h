@@ -85,7 +85,8 @@ hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, 
 hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long sA, const bf16* B,
                           long ldb, long sB, float* out, float* partials, hipStream_t s);
 size_t tn_partial_bytes(int batch, int D, int T);
-// two such reductions in one launch (D a multiple of 256, sA = sB = D):
+// two such reductions in one launch (D = 64, 128 or a multiple of 256,
+// sA = sB = D):
 // out0 over nb0 blocks of (A0, B0), out1 over nb1 blocks of (A1, B1);
 // partials: tn_partial_bytes(nb0 + nb1, D, T) bytes.  Only where that
 // launch splits the tokens (mfma_tn2_ok).
