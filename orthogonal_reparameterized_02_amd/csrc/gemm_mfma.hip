@@ -1034,10 +1034,19 @@ hipError_t blocks_launch(int nblk, int T, int width, const bf16* A, const bf16* 
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
+  // token splits per block: each workgroup loads its G_j (about two token
+  // tiles' time) and then streams its tiles, one workgroup per CU, so the
+  // time goes as rounds of workgroups x (tiles each + 2); take the cheapest
+  // (56 blocks: 4 splits in one round rather than 5 in two)
   const int tiles = (T + TOK - 1) / TOK;
-  const int want = std::max(1, std::min(tiles, (NUM_CU + nblk - 1) / nblk));
-  const int per = (tiles + want - 1) / want;
-  const int splits = (tiles + per - 1) / per;
+  int per = tiles, splits = 1;
+  long best = -1;
+  for (int want = 1; want <= tiles; ++want) {
+    const int p = (tiles + want - 1) / want, sp = (tiles + p - 1) / p;
+    const long rounds = ((long)nblk * sp + NUM_CU - 1) / NUM_CU;
+    const long cost = rounds * (p + 2);
+    if (best < 0 || cost < best || (cost == best && sp < splits)) best = cost, per = p, splits = sp;
+  }
   hipLaunchKernelGGL(kern, dim3(nblk, splits), dim3(64 * WM * WN), lds, s, T, width, per, A, G,
                      Out);
   return hipGetLastError();
