@@ -66,6 +66,12 @@ def test_cnp_argument_errors():
     assert L.poetx_cnp_bwd(4, 256, 4, FAKE, FAKE, FAKE, 0, 1, FAKE,
                            L.poetx_cnp_workspace_bytes(4, 256, 4, 1, 1) - 1, None) == 3
     assert L.poetx_cnp_bwd(4, 32, 4, FAKE, None, FAKE, 0, 0, FAKE, 1 << 20, None) == 1
+    # the backward after the forward checks its arguments the same way
+    assert L.poetx_cnp_bwd_after_fwd(4, 256, 4, FAKE, FAKE, FAKE, 0, 1, FAKE,
+                                     L.poetx_cnp_workspace_bytes(4, 256, 4, 1, 1) - 1, None) == 3
+    assert b"poetx_cnp_bwd_after_fwd" in L.poetx_last_error()
+    assert L.poetx_cnp_bwd_after_fwd(4, 256, 4, FAKE, None, FAKE, 0, 1, FAKE, 1 << 30, None) == 1
+    assert L.poetx_cnp_bwd_after_fwd(4, 7, 4, FAKE, FAKE, FAKE, 0, 1, FAKE, 1 << 30, None) == 1
     assert L.poetx_cnp_workspace_bytes(4, 7, 4, 0, 1) == 0
 
 
