@@ -560,13 +560,15 @@ __device__ __forceinline__ bf16x8_t frag_tr(const char* p0, const char* p1) {
 // 2 * (token % 4), so the four rows one read touches fall on distinct banks.
 // Output: an fp32 TILE x TILE partial, staged through LDS for 16-byte stores.
 // One launch can serve two operand pairs of the same D (dG_R and dG_P):
-// batch entries below nb0 read (A0, B0), the rest (A1, B1).
+// batch entries below nb0 read (A0, B0), the rest (A1, B1).  With one token
+// split and P1 set, the second pair writes its sums to P1 instead of after
+// the first pair's in P (two output buffers, no reduction pass).
 template <int TILE>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_tn4(
     int T, int tsplit, int tiles1, const bf16* __restrict__ A0, long lda0, long sA,
     const bf16* __restrict__ B0, long ldb0, long sB, float* __restrict__ P, long ldp, long sP,
     long sS, int nb0, const bf16* __restrict__ A1, long lda1, const bf16* __restrict__ B1,
-    long ldb1) {
+    long ldb1, float* __restrict__ P1) {
   constexpr int WT = TILE / 2, FM = WT / 32, FN = WT / 32, NF = FM + FN;
   constexpr int MPG = FM * FN / NF;               // MFMAs per group
   constexpr int ROWB_T = TILE * 2;                // LDS bytes per token row
@@ -586,7 +588,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   const long lda = second ? lda1 : lda0, ldb = second ? ldb1 : ldb0;
   const int s = blockIdx.z;
   const int t_begin = s * tsplit, t_end = min(T, t_begin + tsplit);
-  P += s * sS + (long)blockIdx.y * sP;
+  // P1 set: one token split, each pair straight into its own output
+  P = P1 && second ? P1 + bt * sP : P + s * sS + (long)blockIdx.y * sP;
   const int ntok = max(0, t_end - t_begin);
   const int nk = max(1, (ntok + 31) / 32);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
@@ -1084,7 +1087,7 @@ namespace {
 // entries from nb0 on read (A1, B1).  Writes P[s][batch][D][D].
 hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, long lda0,
                       const bf16* B0, long ldb0, const bf16* A1, long lda1, const bf16* B1,
-                      long ldb1, float* P, hipStream_t s) {
+                      long ldb1, float* P, hipStream_t s, float* P1 = nullptr) {
   constexpr int lds = 4 * 2 * 32 * 256 * 2;  // four stages of 32 tokens x (A, B) rows
   static const hipError_t attr = set_lds(k_tn4<256>, lds);
   if (attr != hipSuccess) return attr;
@@ -1096,7 +1099,7 @@ hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, l
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tn4<256>, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit,
                      tiles1, A0, lda0, (long)D, B0, ldb0, (long)D, P, (long)D, dd, dd * batch, nb0,
-                     A1, lda1, B1, ldb1);
+                     A1, lda1, B1, ldb1, P1);
   return hipGetLastError();
 }
 
@@ -1129,7 +1132,7 @@ hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long
 }
 
 bool mfma_tn2_ok(int nb0, int nb1, int D, int T) {
-  return (D == 64 || D == 128 || D % 256 == 0) && tn_splits(nb0 + nb1, D, T) > 1;
+  return D % 256 == 0 || ((D == 64 || D == 128) && tn_splits(nb0 + nb1, D, T) > 1);
 }
 
 hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long lda0,
@@ -1140,6 +1143,8 @@ hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long 
   const int batch = nb0 + nb1;
   const int S = tn_splits(batch, D, T);
   const long dd = (long)D * D;
+  if (S == 1)  // enough tiles without splitting the tokens: sums straight to out0, out1
+    return tn4_launch(batch, nb0, D, T, 1, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, out0, s, out1);
   hipError_t e;
   if (D >= 256)
     e = tn4_launch(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, partials, s);

@@ -88,8 +88,9 @@ size_t tn_partial_bytes(int batch, int D, int T);
 // two such reductions in one launch (D = 64, 128 or a multiple of 256,
 // sA = sB = D):
 // out0 over nb0 blocks of (A0, B0), out1 over nb1 blocks of (A1, B1);
-// partials: tn_partial_bytes(nb0 + nb1, D, T) bytes.  Only where that
-// launch splits the tokens (mfma_tn2_ok).
+// partials: tn_partial_bytes(nb0 + nb1, D, T) bytes (none when the launch
+// does not split the tokens).  b = 64 and 128 only where it does
+// (mfma_tn2_ok).
 bool mfma_tn2_ok(int nb0, int nb1, int D, int T);
 hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long lda0,
                            const bf16* B0, long ldb0, float* out0, const bf16* A1, long lda1,
