@@ -286,8 +286,9 @@ int32_t poetx_merge(const poetx_shape* sh, const void* W0f, const void* G_R,
  *            3 | W0 product | 4 | P-side blocks | 5 | dG_P | 6 | scatter dx | 7
  * When two stages run in one kernel their shared boundary is recorded
  * twice, back to back.  With bf16 (b >= 64) the dG_R reduction runs in the
- * same launch as dG_P wherever that launch splits the tokens: stage 2..3 is
- * then empty and stage 5..6 holds both.  events = NULL clears the hook.
+ * same launch as dG_P (for b = 64 and 128 only where that launch splits the
+ * tokens): stage 2..3 is then empty and stage 5..6 holds both.
+ * events = NULL clears the hook.
  * Errors: ERR_ARG (events non-NULL and count < 8).
  */
 int32_t poetx_set_stage_events(void* const* events, int32_t count);

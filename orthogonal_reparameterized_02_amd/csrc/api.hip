@@ -288,10 +288,10 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   if ((e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s)) != hipSuccess)
     return dev_fail(e, "R-side blocks (bwd)");
   mark(2, s);
-  // dG_Ri = dS_i^T Z_i.  Where both reductions split the tokens on MFMA,
-  // dG_R waits for dG_P and the two run as one launch: half the fp32
-  // partials of two launches, and one reduction pass (dS and Z stay
-  // untouched in between).
+  // dG_Ri = dS_i^T Z_i.  On the MFMA path dG_R waits for dG_P and the two
+  // run as one launch (mfma_tn2_ok): half the fp32 partials of two launches
+  // and one reduction pass, or none when the launch needs no token split
+  // (dS and Z stay untouched in between).
   bool dg_joint = false;
   if constexpr (sizeof(TS) == 2) dg_joint = mf && mfma_tn2_ok(m / b, n / b, b, T);
   if (!dg_joint && (e = tn<TS>(mf, m / b, b, T, dS, m, Z, m, dG_R, part, s)) != hipSuccess)
