@@ -321,9 +321,10 @@ def test_xmem_parity_small_T(T):
 
 
 # ------------------------------------------------------------------ merge
-@pytest.mark.parametrize("name", ["probe", "mid", "square", "mlp13b"])
+@pytest.mark.parametrize("name", ["probe", "mid", "square", "mlp_up", "mlp13b"])
 def test_merge_matches_oracle_weight(name):
-    """poetx_merge returns R W0 P (the oracle's explicit weight)."""
+    """poetx_merge returns R W0 P (the oracle's explicit weight); mlp_up's
+    56 R-side blocks take the block kernel's one-round token split."""
     cfg = I.CONFIG_BY_NAME[name]
     say(f"merge {name}")
     d = I.make_inputs(cfg, seed=31, T=8, want=("W0", "theta_P", "theta_R", "perm_P", "perm_R"))
