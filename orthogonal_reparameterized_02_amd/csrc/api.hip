@@ -129,9 +129,10 @@ BwdWs bwd_ws(const poetx_shape* sh, bool xmem = false) {
   w.part = w.dU + align_up(T * sh->n * es);
   size_t part = 0;
   if (use_mfma(sh)) {
-    const size_t pr = tn_partial_bytes(sh->m / sh->b, sh->b, sh->T);
-    const size_t pp = tn_partial_bytes(sh->n / sh->b, sh->b, sh->T);
-    const size_t pb = tn_partial_bytes(sh->m / sh->b + sh->n / sh->b, sh->b, sh->T);
+    const long wmax = std::max(sh->m, sh->n);  // the widest operand pitch of each reduction
+    const size_t pr = tn_partial_bytes(sh->m / sh->b, sh->b, sh->T, sh->m);
+    const size_t pp = tn_partial_bytes(sh->n / sh->b, sh->b, sh->T, sh->n);
+    const size_t pb = tn_partial_bytes(sh->m / sh->b + sh->n / sh->b, sh->b, sh->T, wmax);
     part = align_up(std::max(pb, std::max(pr, pp)));
   }
   w.Z = w.part + part;
@@ -293,7 +294,7 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   // and one reduction pass, or none when the launch needs no token split
   // (dS and Z stay untouched in between).
   bool dg_joint = false;
-  if constexpr (sizeof(TS) == 2) dg_joint = mf && mfma_tn2_ok(m / b, n / b, b, T);
+  if constexpr (sizeof(TS) == 2) dg_joint = mf && mfma_tn2_ok(m / b, n / b, b, T, std::max(m, n));
   if (!dg_joint && (e = tn<TS>(mf, m / b, b, T, dS, m, Z, m, dG_R, part, s)) != hipSuccess)
     return dev_fail(e, "dG_R");
   mark(3, s);

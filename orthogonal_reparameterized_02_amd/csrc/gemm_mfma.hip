@@ -1063,8 +1063,9 @@ hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, 
   return hipErrorInvalidValue;
 }
 
-// splits of the token range for a D x D (per batch) reduction
-int tn_splits(int batch, int D, int T) {
+// splits of the token range for a D x D (per batch) reduction whose widest
+// operand has row pitch `width` (elements)
+int tn_splits(int batch, int D, int T, long width) {
   const int BT = D >= 256 ? 256 : (D >= 128 ? 128 : 64);
   const long tiles = (long)batch * (D / BT) * (D / BT);
   // D >= 256 (k_tn4): half the CUs already saturate HBM there, and fewer
@@ -1073,11 +1074,19 @@ int tn_splits(int batch, int D, int T) {
   int S = (int)((want + tiles - 1) / tiles);
   const int max_s = (T + 255) / 256;  // keep >= 256 tokens per split
   S = S < max_s ? S : max_s;
-  return S < 1 ? 1 : S;
+  if (S < 1) S = 1;
+  if (D >= 256 && width > 0) {
+    // k_tn4 addresses a split through one buffer range: its tokens (rounded
+    // up to 32) times the row pitch stay below 2^31 bytes
+    const long tmax = ((1L << 31) - 1) / (2 * width) / 32 * 32;
+    const long smin = tmax > 0 ? ((long)T + tmax - 1) / tmax : T;
+    if (S < smin) S = (int)smin;
+  }
+  return S;
 }
 
-size_t tn_partial_bytes(int batch, int D, int T) {
-  const int S = tn_splits(batch, D, T);
+size_t tn_partial_bytes(int batch, int D, int T, long width) {
+  const int S = tn_splits(batch, D, T, width);
   return S > 1 ? (size_t)S * batch * D * D * sizeof(float) : 0;
 }
 
@@ -1094,7 +1103,8 @@ hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, l
   const long dd = (long)D * D;
   const int tiles1 = D / 256;
   const int tsplit = ((T + S - 1) / S + 31) / 32 * 32;
-  // a split's buffer range (tsplit rows of the widest operand) stays below 2^31 bytes
+  // a split's buffer range (tsplit rows of the widest operand) stays below
+  // 2^31 bytes; tn_splits chose S for that, this only guards the invariant
   if ((long)tsplit * std::max(std::max(lda0, ldb0), std::max(lda1, ldb1)) * 2 >= (1L << 31))
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_tn4<256>, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit,
@@ -1115,7 +1125,7 @@ hipError_t reduce_launch(long n, int S, const float* P, float* out0, long n0, fl
 
 hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long sA, const bf16* B,
                           long ldb, long sB, float* out, float* partials, hipStream_t s) {
-  const int S = tn_splits(batch, D, T);
+  const int S = tn_splits(batch, D, T, std::max(lda, ldb));
   const long dd = (long)D * D;
   float* P = S > 1 ? partials : out;
   hipError_t e;
@@ -1131,17 +1141,18 @@ hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long
   return reduce_launch(dd * batch, S, P, out, dd * batch, nullptr, s);
 }
 
-bool mfma_tn2_ok(int nb0, int nb1, int D, int T) {
-  return D % 256 == 0 || ((D == 64 || D == 128) && tn_splits(nb0 + nb1, D, T) > 1);
+bool mfma_tn2_ok(int nb0, int nb1, int D, int T, long width) {
+  return D % 256 == 0 || ((D == 64 || D == 128) && tn_splits(nb0 + nb1, D, T, width) > 1);
 }
 
 hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long lda0,
                            const bf16* B0, long ldb0, float* out0, const bf16* A1, long lda1,
                            const bf16* B1, long ldb1, float* out1, float* partials,
                            hipStream_t s) {
-  if (!mfma_tn2_ok(nb0, nb1, D, T)) return hipErrorInvalidValue;
+  const long width = std::max(std::max(lda0, ldb0), std::max(lda1, ldb1));
+  if (!mfma_tn2_ok(nb0, nb1, D, T, width)) return hipErrorInvalidValue;
   const int batch = nb0 + nb1;
-  const int S = tn_splits(batch, D, T);
+  const int S = tn_splits(batch, D, T, width);
   const long dd = (long)D * D;
   if (S == 1)  // enough tiles without splitting the tokens: sums straight to out0, out1
     return tn4_launch(batch, nb0, D, T, 1, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, out0, s, out1);

@@ -79,19 +79,19 @@ bool mfma_blocks_ok(int b);
 hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, const bf16* G,
                               bf16* Out, hipStream_t s);
 // out[bt][r][c] = sum_t A[t][bt*sA + r] B[t][bt*sB + c], D x D per batch,
-// D in {64, 128, 256, 512}; partials: tn_partial_bytes(batch, D, T) bytes.
-// D >= 256: sA = sB = D, and one token split of the widest operand spans
-// under 2^31 bytes (else hipErrorInvalidValue)
+// D in {64, 128, 256, 512}; partials: tn_partial_bytes(batch, D, T,
+// max(lda, ldb)) bytes.  D >= 256: sA = sB = D; the token splits are sized
+// so that one split of the widest operand spans under 2^31 bytes.
 hipError_t launch_mfma_tn(int batch, int D, int T, const bf16* A, long lda, long sA, const bf16* B,
                           long ldb, long sB, float* out, float* partials, hipStream_t s);
-size_t tn_partial_bytes(int batch, int D, int T);
+size_t tn_partial_bytes(int batch, int D, int T, long width);
 // two such reductions in one launch (D = 64, 128 or a multiple of 256,
 // sA = sB = D):
 // out0 over nb0 blocks of (A0, B0), out1 over nb1 blocks of (A1, B1);
-// partials: tn_partial_bytes(nb0 + nb1, D, T) bytes (none when the launch
-// does not split the tokens).  b = 64 and 128 only where it does
-// (mfma_tn2_ok).
-bool mfma_tn2_ok(int nb0, int nb1, int D, int T);
+// partials: tn_partial_bytes(nb0 + nb1, D, T, widest pitch) bytes (none
+// when the launch does not split the tokens).  b = 64 and 128 only where it
+// does (mfma_tn2_ok, width = the widest of the four pitches).
+bool mfma_tn2_ok(int nb0, int nb1, int D, int T, long width);
 hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long lda0,
                            const bf16* B0, long ldb0, float* out0, const bf16* A1, long lda1,
                            const bf16* B1, long ldb1, float* out1, float* partials,
