@@ -319,13 +319,13 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
       constexpr int QPF = 2;
       constexpr int NKS = B / 16;
       uint4 bq[2], aq[QPF][RTW];
-      // one row offset per row tile; the K offset (ks * 32 bytes < 1 KB)
-      // becomes the load's immediate offset.  Q is the same in every step,
-      // so the offsets pass through an empty asm each step: otherwise the
-      // compiler hoists all of the wave's Q loads out of the step loop and
-      // tries to keep its 64 KB of Q in registers.  (An offset, not the
-      // pointer: a pointer through asm loses its global address space and
-      // the loads become flat ones, which also count against lgkmcnt.)
+      // one element offset per row tile (its K-step 0 fragment; K-step ks
+      // lies ks KB further).  Q is the same in every step, so the offsets
+      // pass through an empty asm each step: otherwise the compiler hoists
+      // all of the wave's Q loads out of the step loop and tries to keep its
+      // 64 KB of Q in registers.  (An offset, not the pointer: a pointer
+      // through asm loses its global address space and the loads become
+      // flat ones, which also count against lgkmcnt.)
       int qoff[RTW];
 #pragma unroll
       for (int t = 0; t < RTW; ++t) {
