@@ -917,13 +917,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
 
 
 // out[e] = sum_{s < S} P[s * stride + e], fixed order
+// (n, n0 and stride multiples of 4 and every buffer 16-byte aligned: the
+// sums go four at a time, each still in split order)
 __global__ void k_reduce_splits(long n, int S, long stride, const float* __restrict__ P,
                                 float* __restrict__ out, long n0, float* __restrict__ out1) {
-  for (long e = (long)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
-    float acc = P[e];
-    for (int s = 1; s < S; ++s) acc += P[s * stride + e];
-    if (e < n0) out[e] = acc;
-    else out1[e - n0] = acc;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  for (long e = ((long)blockIdx.x * blockDim.x + threadIdx.x) * 4; e < n;
+       e += (long)gridDim.x * blockDim.x * 4) {
+    f32x4 acc = *reinterpret_cast<const f32x4*>(P + e);
+    for (int s = 1; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(P + s * stride + e);
+    if (e < n0) *reinterpret_cast<f32x4*>(out + e) = acc;
+    else *reinterpret_cast<f32x4*>(out1 + (e - n0)) = acc;
   }
 }
 
@@ -1116,7 +1120,8 @@ hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, l
 // out0 = the first n0 sums over S partials of stride n, out1 = the rest
 hipError_t reduce_launch(long n, int S, const float* P, float* out0, long n0, float* out1,
                          hipStream_t s) {
-  const int grid = (int)std::min<long>((n + 255) / 256, 4096);
+  if (n % 4 || n0 % 4) return hipErrorInvalidValue;
+  const int grid = (int)std::min<long>((n / 4 + 255) / 256, 4096);
   hipLaunchKernelGGL(k_reduce_splits, dim3(grid), dim3(256), 0, s, n, S, n, P, out0, n0, out1);
   return hipGetLastError();
 }
