@@ -181,11 +181,13 @@ def test_layer_parity_small_T(name):
 
 
 @pytest.mark.parametrize("name,T,k", [("square", 1, 4), ("square", 257, 4), ("mid", 33, 0),
-                                      ("mid", 4063, 4), ("mlp13b", 1, 5), ("probe", 1, 0)])
+                                      ("mid", 4063, 4), ("mlp_up", 4100, 4), ("mlp13b", 1, 5),
+                                      ("probe", 1, 0)])
 def test_layer_edge_cases(name, T, k):
     """One token, a ragged tail just past a 256-token tile, a ragged last
-    tile on the unfused 256 x 256 dense path (mid, 128 tiles), and k = 0
-    (G = I + Q): every output against the oracle."""
+    tile on the 256 x 256 dense path (mid, 128 tiles), uneven token splits
+    of the 56-block pass and the joint 72-block dG reduction (mlp_up), and
+    k = 0 (G = I + Q): every output against the oracle."""
     base = I.CONFIG_BY_NAME[name]
     cfg = I.LayerConfig(base.name, base.m, base.n, base.b, k, T, base.dtype, base.sigma)
     say(f"edge {name} T={T} k={k}")
