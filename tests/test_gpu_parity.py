@@ -277,7 +277,7 @@ def test_repeat_runs_bitwise_equal():
 
 # ------------------------------------------------------------------ xmem mode
 @pytest.mark.parametrize("name,T", [("probe", 64), ("mid", 200), ("square", 96),
-                                    ("mlp13b", 40), ("square", 8192)])
+                                    ("mlp13b", 40), ("square", 8192), ("mlp_up", 600)])
 def test_xmem_bitwise_equals_xfast(name, T):
     """The memory-saving mode keeps only U and recomputes Z in the backward
     with the forward's own kernels, so every output equals the default
