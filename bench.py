@@ -42,7 +42,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="square")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=8192)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--xmem", action="store_true",
                     help="memory-saving mode: keep only U, recompute Z in the backward")
@@ -269,32 +269,44 @@ def measured_traffic(config_name: str):
         return None
 
 
-def cpu_baseline(cfg, seed: int, ts: int, min_s: float = 10.0, max_reps: int = 4) -> dict:
+def cpu_baseline(cfg, seed: int, ts: int, reps: int = 3, warmup: int = 1) -> dict:
     """The float64 oracle, as it stands, on the first `ts` tokens of the same
-    workload: forward and backward (weights formed, CNP both sides), repeated
-    until at least `min_s` seconds of CPU work (at most `max_reps` passes)."""
+    workload: forward and backward (weights formed, CNP both sides), `warmup`
+    untimed passes and then the median of `reps` timed ones.  Reports the
+    BLAS library and the threads it ran with."""
     import numpy as np
+    blas, cores = "unknown", len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            blas = f"{libs[0].get('internal_api', '?')} {libs[0].get('version', '')}".strip()
+            cores = max(i.get("num_threads", 1) for i in libs)
     except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
+        pass
     import oracle as O
     from orthogonal_reparameterized_02_amd import inputs as I
     d = I.make_inputs(cfg, seed=seed, T=ts)
-    reps, t = 0, time.perf_counter()
-    while True:
+
+    def one_pass():
         O.layer_fwd(d["x64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
                     d["perm_R"], cfg.b, cfg.k)
         O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"],
                     d["perm_P"], d["perm_R"], cfg.b, cfg.k)
-        reps += 1
-        dt = time.perf_counter() - t
-        if dt >= min_s or reps >= max_reps:
-            break
-    return {"value": reps * ts / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {ts} of {cfg.T} tokens of the same layer, forward+backward "
-                      f"{reps}x in float64 NumPy ({dt:.1f} s)"}
+
+    for _ in range(warmup):
+        one_pass()
+    times = []
+    for _ in range(reps):
+        t = time.perf_counter()
+        one_pass()
+        times.append(time.perf_counter() - t)
+    med = float(np.median(times))
+    return {"value": ts / med, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "blas": blas,
+            "sample": f"first {ts} of {cfg.T} tokens of the same layer, forward+backward in "
+                      f"float64 NumPy: {warmup} warm-up pass, median of {reps} timed passes "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s)"}
 
 
 if __name__ == "__main__":

@@ -241,6 +241,63 @@ def layer_bwd(x, dy, W0, theta_P, theta_R, perm_P, perm_R, b, k):
 
 
 # --------------------------------------------------------------------------
+# bilinear probes of dG, for token counts where dG itself is too costly
+# --------------------------------------------------------------------------
+def dG_probes(x, dy, W0, G_P, G_R, perm_P, perm_R, u_P, v_P, u_R, v_R):
+    """u^T dG v for every block and probe pair, without forming dG.
+
+    With U = x[:, pi_P], V_j = U_j G_Pj^T, Z = V W0f^T, dS = dy[:, pi_R],
+    dZ_i = dS_i G_Ri, dV = dZ W0f (the input-centric form, [X-zh] 2.1-2.3):
+      dG_Ri = sum_t dS_i[t]^T Z_i[t]   ->  u^T dG_Ri v = sum_t (dS_i[t].u)(Z_i[t].v)
+      dG_Pj = sum_t dV_j[t]^T U_j[t]   ->  u^T dG_Pj v = sum_t (dV_j[t].u)(U_j[t].v)
+    Each per-token dot product is linear in x[t] or dy[t], so it is x[t] or
+    dy[t] against one fixed vector, found by pulling the probe back through
+    the layer's maps:
+      Z_i[t].v  = V[t].(W0f_i^T v)  = sum_j U_j[t].(G_Pj^T w_j) = x[t].rx
+      dS_i[t].u = dy[t].ry          (u placed at columns pi_R[i b + c])
+      U_j[t].v  = x[t].rx'          (v placed at columns pi_P[j b + c])
+      dV_j[t].u = dZ[t].(W0f_{:,j} u) = sum_i dS_i[t].(G_Ri s_i) = dy[t].ry'
+    so every probe of every block is one column of x @ Rx times one column
+    of dy @ Ry, summed over tokens.  u_P, v_P: [probes, N_P, b];
+    u_R, v_R: [probes, N_R, b].  Returns (probes_P [probes, N_P],
+    probes_R [probes, N_R]) in float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    perm_P = np.asarray(perm_P)
+    perm_R = np.asarray(perm_R)
+    W0f, _, _ = fold_perm(np.asarray(W0, dtype=np.float64), perm_R, perm_P)
+    m, n = W0f.shape
+    b = G_P.shape[1]
+    npr, nP, nR = u_P.shape[0], n // b, m // b
+    Rx = np.zeros((n, npr * (nR + nP)))   # columns: R-side Z.v, then P-side U.v
+    Ry = np.zeros((m, npr * (nR + nP)))   # columns: R-side dS.u, then P-side dV.u
+    col = 0
+    for q in range(npr):
+        for i in range(nR):
+            I = slice(i * b, (i + 1) * b)
+            w = W0f[I].T @ v_R[q, i]                       # n, in U coordinates
+            r = np.concatenate([G_P[j].T @ w[j * b:(j + 1) * b] for j in range(nP)])
+            Rx[perm_P, col] = r                            # U[t].r = x[t].Rx[:, col]
+            Ry[perm_R[I], col] = u_R[q, i]                 # dS_i[t].u = dy[t].Ry[:, col]
+            col += 1
+    for q in range(npr):
+        for j in range(nP):
+            J = slice(j * b, (j + 1) * b)
+            Rx[perm_P[J], col] = v_P[q, j]                 # U_j[t].v
+            s_ = W0f[:, J] @ u_P[q, j]                     # m, in dZ coordinates
+            r = np.concatenate([G_R[i] @ s_[i * b:(i + 1) * b] for i in range(nR)])
+            Ry[perm_R, col] = r                            # dS[t].r = dy[t].Ry[:, col]
+            col += 1
+    acc = np.zeros(col)
+    for s0 in range(0, x.shape[0], CHUNK):
+        acc += np.sum((x[s0:s0 + CHUNK] @ Rx) * (dy[s0:s0 + CHUNK] @ Ry), axis=0)
+    probes_R = acc[:npr * nR].reshape(npr, nR)
+    probes_P = acc[npr * nR:].reshape(npr, nP)
+    return probes_P, probes_R
+
+
+# --------------------------------------------------------------------------
 # second formulation: input-centric with two permutations folded into W0
 # ([X-zh] 2.1 "input-centric", 2.2 "4 -> 2 permutations", 2.3 batched blocks)
 # --------------------------------------------------------------------------
@@ -294,8 +351,50 @@ def weight_dense(W0, G_R, G_P, perm_R, perm_P) -> np.ndarray:
 # comparison metric used by the parity tests
 # --------------------------------------------------------------------------
 def rel_fro(got: np.ndarray, ref: np.ndarray) -> float:
-    """||got - ref||_F / ||ref||_F in float64."""
+    """||got - ref||_F / ||ref||_F in float64 (the plain difference when ref
+    is all zero)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    den = np.linalg.norm(ref)
-    return float(np.linalg.norm(got - ref) / (den if den > 0 else 1.0))
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    den = np.sqrt(np.sum(ref * ref))
+    num = np.sqrt(np.sum((got - ref) * (got - ref)))
+    return float(num / (den if den > 0 else 1.0))
+
+
+def max_ratio(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref| over all elements, in float64 (the plain
+    largest difference when ref is all zero).  One wrong element among many
+    shows here at full size, where a norm over the whole tensor dilutes it."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if got.size == 0:
+        return 0.0
+    den = np.abs(ref).max()
+    return float(np.abs(got - ref).max() / (den if den > 0 else 1.0))
+
+
+def rel_fro_slices(got: np.ndarray, ref: np.ndarray, axis: int = 0) -> np.ndarray:
+    """rel_fro of every slice along `axis`: entry i compares
+    got.take(i, axis) with ref.take(i, axis).  axis 0 of a [N, ...] block
+    tensor gives one figure per orthogonal block (each block is an
+    independent matrix, [X-zh] 2.3); axis 0 / 1 of a token-major [T, w]
+    activation gives one per token / per feature."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    return np.array([rel_fro(got.take(i, axis), ref.take(i, axis))
+                     for i in range(got.shape[axis])])
+
+
+# --------------------------------------------------------------------------
+# int8 base weight ([X-zh] 2.6; [X-it] 2: training on a quantized base
+# model, dequantized when needed)
+# --------------------------------------------------------------------------
+def dequant_rows(q: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """The float64 weight an int8 matrix q with one scale per output row
+    stands for: W0[i, j] = s[i] * q[i, j] (exact in float64)."""
+    q = np.asarray(q)
+    s = np.asarray(s)
+    assert q.ndim == 2 and s.shape == (q.shape[0],)
+    return s.astype(np.float64)[:, None] * q.astype(np.float64)

@@ -150,7 +150,3 @@ def quantize_rows_int8(w: np.ndarray):
     q = np.clip(np.rint(w / s.astype(np.float64)[:, None]), -127, 127).astype(np.int8)
     return q, s
 
-
-def dequantized(q: np.ndarray, s: np.ndarray) -> np.ndarray:
-    """The float64 weight an int8 (q, s) pair represents."""
-    return s.astype(np.float64)[:, None] * q.astype(np.float64)

@@ -163,59 +163,122 @@ class POETXLayer:
 
 
 class _POETXFn(torch.autograd.Function):
+    """One call of the layer.  Every forward call owns its G, G^T, saved
+    activations, CNP workspace (which keeps the call's unpacked Q) and
+    a snapshot of theta, all from torch's caching allocator, so forwards may
+    run back to back before their backwards (micro-batch accumulation,
+    weight tying) and each backward sees its own forward's state."""
+
     @staticmethod
-    def forward(ctx, x, theta_P, theta_R, layer: POETXLayer):
-        layer.set_theta(theta_P.detach(), theta_R.detach())
-        y = layer.forward(x.contiguous()).clone()
-        ctx.layer = layer
-        return y
+    def forward(ctx, x, theta_P, theta_R, mod: "POETXLinear"):
+        n, m, b, k, act = mod.n, mod.m, mod.b, mod.k, mod.act
+        if x.shape[-1] != n:
+            raise ValueError(f"x has {x.shape[-1]} features, the layer takes n={n}")
+        if x.dtype != mod.dtype:
+            raise ValueError(f"x has dtype {x.dtype}, the layer computes in {mod.dtype}")
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, n).contiguous()
+        T = x2.shape[0]
+        if T < 1:
+            raise ValueError("x holds no tokens")
+        dev, dt = x2.device, mod.dtype
+        sh = P.shape(m, n, b, k, T, act)
+        nP = n // b
+        theta = torch.cat([theta_P.detach(), theta_R.detach()]).to(torch.float32).contiguous()
+        nb = theta.shape[0]
+        G = torch.empty(nb, b, b, dtype=dt, device=dev)
+        GT = torch.empty_like(G)
+        ws_cnp = _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 1, act), dev)
+        P.poetx_cnp_fwd(theta, b, k, G, GT, ws_cnp)
+        y = torch.empty(T, m, dtype=dt, device=dev)
+        saved = _bytes(P.poetx_saved_bytes(sh), dev)
+        ws = _bytes(P.poetx_workspace_bytes(sh, 0), dev)
+        P.poetx_layer_fwd(sh, x2, G[:nP], G[nP:], mod.W0f, mod.perm_P, mod.perm_R_inv, y, saved,
+                          ws)
+        del ws, G
+        ctx.mod, ctx.sh, ctx.lead = mod, sh, lead
+        ctx.state = (theta, GT, saved, ws_cnp)
+        return y.reshape(*lead, m)
 
     @staticmethod
     def backward(ctx, dy):
-        L = ctx.layer
-        dx, dP, dR = L.backward(dy.to(L.dtype).contiguous())
-        return dx.clone(), dP.clone(), dR.clone(), None
+        mod, sh = ctx.mod, ctx.sh
+        theta, GT, saved, ws_cnp = ctx.state
+        ctx.state = None
+        n, m, b, k, act, T = mod.n, mod.m, mod.b, mod.k, mod.act, sh.T
+        dev = dy.device
+        dy2 = dy.reshape(T, m).to(mod.dtype).contiguous()
+        nP = n // b
+        dx = torch.empty(T, n, dtype=mod.dtype, device=dev)
+        dG = torch.empty(theta.shape[0], b, b, dtype=torch.float32, device=dev)
+        ws = _bytes(P.poetx_workspace_bytes(sh, 1), dev)
+        P.poetx_layer_bwd(sh, dy2, GT[:nP], GT[nP:], mod.W0fT, mod.perm_P_inv, mod.perm_R, saved,
+                          dx, dG[:nP], dG[nP:], ws)
+        del ws
+        dtheta = torch.empty_like(theta)
+        # ws_cnp still holds this call's own unpacked Q
+        P.poetx_cnp_bwd(theta, dG, b, k, dtheta, act, ws=ws_cnp, after_fwd=True)
+        return dx.reshape(*ctx.lead, n), dtheta[:nP], dtheta[nP:], None
 
 
 class POETXLinear(torch.nn.Module):
     """y = x (R W0 P)^T with a fixed random W0 and CNP-parameterized R, P.
 
     theta_P / theta_R start at 0 (R = P = I, the layer equals W0).
-    `start_inner_loop()` draws new permutations and folds them into W0.
-    One module serves one token count T (its workspaces are sized for it).
+    `start_inner_loop()` draws new permutations and folds them into W0;
+    `end_inner_loop()` merges the learned transforms into W0 first.
+    x is [..., n] in the layer's dtype, any number of tokens per call; each
+    call is independent of the others (see _POETXFn).
     """
 
-    def __init__(self, n: int, m: int, b: int, k: int, T: int, dtype=torch.bfloat16,
-                 seed: int = 0, device="cuda"):
+    def __init__(self, n: int, m: int, b: int, k: int, dtype=torch.bfloat16, seed: int = 0,
+                 device="cuda"):
         super().__init__()
-        act = P.act_of(dtype)
+        self.n, self.m, self.b, self.k = n, m, b, k
+        self.act, self.dtype = P.act_of(dtype), dtype
+        # shape checks of the library (T is free here, 1 stands in)
+        if P.poetx_saved_bytes(P.shape(m, n, b, k, 1, self.act)) == 0:
+            raise ValueError(f"unsupported layer m={m} n={n} b={b} k={k} {dtype}: "
+                             + P.lib().poetx_last_error().decode())
         g = torch.Generator().manual_seed(seed)
         self.register_buffer("W0", (torch.randn(m, n, generator=g) / n ** 0.5).to(dtype).to(device))
         tb = b * (b - 1) // 2
         self.theta_P = torch.nn.Parameter(torch.zeros(n // b, tb, device=device))
         self.theta_R = torch.nn.Parameter(torch.zeros(m // b, tb, device=device))
-        self._layer = POETXLayer(m, n, b, k, T, act, device)
+        e = lambda *s, d=dtype: torch.empty(*s, dtype=d, device=device)
+        self.W0f, self.W0fT = e(m, n), e(n, m)
+        self.perm_P, self.perm_R = e(n, d=torch.int32), e(m, d=torch.int32)
+        self.perm_P_inv, self.perm_R_inv = e(n, d=torch.int32), e(m, d=torch.int32)
         self._gen = g
         self.start_inner_loop()
 
     def start_inner_loop(self) -> None:
-        pP = torch.randperm(self._layer.n, generator=self._gen).to(torch.int32)
-        pR = torch.randperm(self._layer.m, generator=self._gen).to(torch.int32)
-        self._layer.load(self.W0, self.theta_P.detach(), self.theta_R.detach(),
-                         pP.to(self.W0.device), pR.to(self.W0.device))
+        """Draw new permutations and fold them into the weight."""
+        self.perm_P.copy_(torch.randperm(self.n, generator=self._gen).to(torch.int32))
+        self.perm_R.copy_(torch.randperm(self.m, generator=self._gen).to(torch.int32))
+        P.poetx_fold_perm(self.W0, self.perm_R, self.perm_P, self.W0f, self.W0fT,
+                          self.perm_R_inv, self.perm_P_inv)
 
     @torch.no_grad()
     def end_inner_loop(self) -> None:
         """Merge the learned transforms into the weight (W0 <- R W0 P), reset
         theta to 0 (R = P = I) and start a new inner loop with new
         permutations; the layer's function is unchanged by the merge."""
-        L = self._layer
-        L.set_theta(self.theta_P, self.theta_R)
-        L.cnp()
-        self.W0.copy_(L.merge())
+        n, m, b, k, act = self.n, self.m, self.b, self.k, self.act
+        theta = torch.cat([self.theta_P, self.theta_R]).float().contiguous()
+        nb, nP = theta.shape[0], n // b
+        G = torch.empty(nb, b, b, dtype=self.dtype, device=theta.device)
+        GT = torch.empty_like(G)
+        P.poetx_cnp_fwd(theta, b, k, G, GT, _bytes(P.poetx_cnp_workspace_bytes(nb, b, k, 0, act),
+                                                   theta.device))
+        sh = P.shape(m, n, b, k, 1, act)
+        W = torch.empty(m, n, dtype=self.dtype, device=theta.device)
+        P.poetx_merge(sh, self.W0f, G[nP:], GT[:nP], self.perm_R_inv, self.perm_P_inv, W,
+                      _bytes(P.poetx_workspace_bytes(sh, 4), theta.device))
+        self.W0.copy_(W)
         self.theta_P.zero_()
         self.theta_R.zero_()
         self.start_inner_loop()
 
     def forward(self, x: torch.Tensor) -> torch.Tensor:
-        return _POETXFn.apply(x, self.theta_P, self.theta_R, self._layer)
+        return _POETXFn.apply(x, self.theta_P, self.theta_R, self)

@@ -40,3 +40,42 @@ def raw(a: np.ndarray) -> np.ndarray:
 
 def act_of(dtype: str) -> int:
     return 1 if dtype == "bf16" else 0
+
+
+def check_close(name, got, ref, tol, *, rows=False, cols=False, blocks=False, log=None):
+    """Bound a GPU result (float64 host array) against the oracle's with the
+    same `tol` on every figure:
+      fro    ||got - ref||_F / ||ref||_F over the whole tensor;
+      max    max |got - ref| / max |ref|;
+      block  the worst rel-Fro of one block ([N, ...] block tensors:
+             G, dG, dtheta; each block is an independent matrix);
+      row    the worst rel-Fro of one token row ([T, w] activations);
+      col    the worst rel-Fro of one feature column over the tokens
+             (only with at least 32 tokens, where a column norm is stable).
+    Returns the figures; raises AssertionError naming those over `tol`."""
+    import oracle as O
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    errs = {"fro": O.rel_fro(got, ref), "max": O.max_ratio(got, ref)}
+    if blocks:
+        errs["block"] = float(O.rel_fro_slices(got, ref, 0).max())
+    if rows:
+        errs["row"] = float(O.rel_fro_slices(got, ref, 0).max())
+    if cols and got.shape[0] >= 32:
+        errs["col"] = float(O.rel_fro_slices(got, ref, 1).max())
+    if log is not None:
+        log(f"  {name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    bad = {k: v for k, v in errs.items() if not v <= tol}
+    assert not bad, f"{name}: {bad} over {tol} (all: {errs})"
+    return errs
+
+
+def check_layer(out, ref, tol, log=None, rows_only=False):
+    """check_close over a layer's outputs: y and dx per token row and per
+    feature column, dG and dtheta per block.  `out` and `ref` map names to
+    float64 arrays; names missing from either side are skipped."""
+    for nm in ("y", "dx", "dG_P", "dG_R", "dtheta_P", "dtheta_R"):
+        if nm in out and nm in ref:
+            act = nm in ("y", "dx")
+            check_close(nm, out[nm], ref[nm], tol, rows=act, cols=act and not rows_only,
+                        blocks=not act, log=log)

@@ -1,6 +1,9 @@
 """GPU parity: the HIP path through the C ABI against the float64 oracle on
-the same seeded inputs.  Index work must be bit-exact; floating point within
-1e-5 (float32) or 2e-2 (bf16 storage) relative Frobenius error."""
+the same seeded inputs.  Index work must be bit-exact.  Floating point is
+held to 1e-5 (float32) or 2e-2 (bf16 storage) on every figure check_close
+takes: relative Frobenius error of the whole tensor, of each block (G, dG,
+dtheta), of each token row and feature column (y, dx), and
+max |gpu - ref| / max |ref|."""
 import sys
 
 import numpy as np
@@ -8,7 +11,7 @@ import pytest
 import torch
 
 import oracle as O
-from gpu_util import TOL, act_of, bits, raw, to_dev, to_f64
+from gpu_util import TOL, act_of, bits, check_close, check_layer, raw, to_dev, to_f64
 from orthogonal_reparameterized_02_amd import inputs as I
 from orthogonal_reparameterized_02_amd import poetx as P
 from orthogonal_reparameterized_02_amd.layer import POETXLayer
@@ -87,9 +90,7 @@ def test_cnp_fwd(nblk, b, k, dtype, sigma):
     P.poetx_cnp_fwd(to_dev(th), b, k, G, GT, ws)
     torch.cuda.synchronize()
     ref = O.cnp_fwd(th.astype(np.float64), b, k)
-    err = O.rel_fro(to_f64(G), ref)
-    say(f"  rel err {err:.3e}")
-    assert err <= TOL[dtype]
+    check_close("G", to_f64(G), ref, TOL[dtype], blocks=True, log=say)
     np.testing.assert_array_equal(bits(GT), bits(G).transpose(0, 2, 1))
 
 
@@ -109,9 +110,7 @@ def test_cnp_bwd(nblk, b, k, dtype, sigma, accumulate):
     got = to_f64(dth)
     if accumulate:
         got = got - prior.astype(np.float64)
-    err = O.rel_fro(got, ref)
-    say(f"  rel err {err:.3e}")
-    assert err <= TOL[dtype]
+    check_close("dtheta", got, ref, TOL[dtype], blocks=True, log=say)
 
 
 @pytest.mark.parametrize("accumulate", [False, True])
@@ -151,6 +150,14 @@ def run_layer(cfg, d, T):
     return L
 
 
+def layer_out(L, rows=None):
+    """The layer's outputs as float64 host arrays (y and dx restricted to
+    `rows` when given)."""
+    sel = (lambda t: t) if rows is None else (lambda t: t[torch.as_tensor(rows, device="cuda")])
+    return {"y": to_f64(sel(L.y)), "dx": to_f64(sel(L.dx)), "dG_P": to_f64(L.dG_P),
+            "dG_R": to_f64(L.dG_R), "dtheta_P": to_f64(L.dtheta_P), "dtheta_R": to_f64(L.dtheta_R)}
+
+
 SMALL_T = {"probe": 64, "mid": 200, "square": 96, "mlp_up": 64, "mlp13b": 40}
 
 
@@ -167,17 +174,7 @@ def test_layer_parity_small_T(name):
                            d["perm_R"], cfg.b, cfg.k)
     g = O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
                     d["perm_R"], cfg.b, cfg.k)
-    errs = {
-        "y": O.rel_fro(to_f64(L.y), y_ref),
-        "dx": O.rel_fro(to_f64(L.dx), g["dx"]),
-        "dG_P": O.rel_fro(to_f64(L.dG_P), g["dG_P"]),
-        "dG_R": O.rel_fro(to_f64(L.dG_R), g["dG_R"]),
-        "dtheta_P": O.rel_fro(to_f64(L.dtheta_P), g["dtheta_P"]),
-        "dtheta_R": O.rel_fro(to_f64(L.dtheta_R), g["dtheta_R"]),
-    }
-    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, v in errs.items():
-        assert v <= TOL[cfg.dtype], (k, v)
+    check_layer(layer_out(L), dict(g, y=y_ref), TOL[cfg.dtype], log=say)
 
 
 @pytest.mark.parametrize("name,T,k", [("square", 1, 4), ("square", 257, 4), ("mid", 33, 0),
@@ -197,11 +194,7 @@ def test_layer_edge_cases(name, T, k):
                            d["perm_R"], cfg.b, cfg.k)
     g = O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
                     d["perm_R"], cfg.b, cfg.k)
-    for nm, got, ref in (("y", L.y, y_ref), ("dx", L.dx, g["dx"]),
-                         ("dtheta_P", L.dtheta_P, g["dtheta_P"]),
-                         ("dtheta_R", L.dtheta_R, g["dtheta_R"])):
-        err = O.rel_fro(to_f64(got), ref)
-        assert err <= TOL[cfg.dtype], (nm, err)
+    check_layer(layer_out(L), dict(g, y=y_ref), TOL[cfg.dtype], log=say)
 
 
 @pytest.mark.parametrize("name", ["mid", "square", "mlp_up", "mlp13b"])
@@ -218,19 +211,12 @@ def test_layer_parity_full_size(name):
     G_P = O.cnp_fwd(d["theta_P64"], cfg.b, cfg.k)
     G_R = O.cnp_fwd(d["theta_R64"], cfg.b, cfg.k)
     W = O.weight(d["W064"], G_R, G_P, d["perm_R"], d["perm_P"])
-    y_rows = to_f64(L.y[torch.as_tensor(rows, device="cuda")])
-    dx_rows = to_f64(L.dx[torch.as_tensor(rows, device="cuda")])
-    e_y = O.rel_fro(y_rows, d["x64"][rows] @ W.T)
-    e_dx = O.rel_fro(dx_rows, d["dy64"][rows] @ W)
-    say(f"  y rows {e_y:.2e}  dx rows {e_dx:.2e}")
-    assert e_y <= TOL[cfg.dtype] and e_dx <= TOL[cfg.dtype]
+    ref = {"y": d["x64"][rows] @ W.T, "dx": d["dy64"][rows] @ W}
     del W
     g = O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
                     d["perm_R"], cfg.b, cfg.k)
-    e_p = O.rel_fro(to_f64(L.dtheta_P), g["dtheta_P"])
-    e_r = O.rel_fro(to_f64(L.dtheta_R), g["dtheta_R"])
-    say(f"  dtheta_P {e_p:.2e}  dtheta_R {e_r:.2e}")
-    assert e_p <= TOL[cfg.dtype] and e_r <= TOL[cfg.dtype]
+    ref.update({nm: g[nm] for nm in ("dG_P", "dG_R", "dtheta_P", "dtheta_R")})
+    check_layer(layer_out(L, rows), ref, TOL[cfg.dtype], log=say)
 
 
 @pytest.mark.parametrize("dtype,b", [("bf16", 256), ("bf16", 128), ("bf16", 32), ("f32", 32)])
@@ -317,9 +303,7 @@ def test_xmem_parity_small_T(T):
                            d["perm_R"], cfg.b, cfg.k)
     g = O.layer_bwd(d["x64"], d["dy64"], d["W064"], d["theta_P64"], d["theta_R64"], d["perm_P"],
                     d["perm_R"], cfg.b, cfg.k)
-    for got, ref in ((L.y, y_ref), (L.dx, g["dx"]), (L.dtheta_P, g["dtheta_P"]),
-                     (L.dtheta_R, g["dtheta_R"])):
-        assert O.rel_fro(to_f64(got), ref) <= TOL[cfg.dtype]
+    check_layer(layer_out(L), dict(g, y=y_ref), TOL[cfg.dtype], log=say)
 
 
 # ------------------------------------------------------------------ merge
@@ -339,9 +323,7 @@ def test_merge_matches_oracle_weight(name):
     G_P = O.cnp_fwd(d["theta_P64"], cfg.b, cfg.k)
     G_R = O.cnp_fwd(d["theta_R64"], cfg.b, cfg.k)
     ref = O.weight(d["W064"], G_R, G_P, d["perm_R"], d["perm_P"])
-    err = O.rel_fro(to_f64(W), ref)
-    say(f"  rel err {err:.2e}")
-    assert err <= TOL[cfg.dtype]
+    check_close("W", to_f64(W), ref, TOL[cfg.dtype], rows=True, cols=True, log=say)
 
 
 @pytest.mark.parametrize("name", ["probe", "square"])
@@ -364,21 +346,19 @@ def test_end_inner_loop_keeps_the_function():
     computes the same function as before (to bf16 rounding)."""
     from orthogonal_reparameterized_02_amd.layer import POETXLinear
     torch.manual_seed(1)
-    mod = POETXLinear(n=512, m=768, b=128, k=4, T=64, dtype=torch.bfloat16, seed=4)
+    mod = POETXLinear(n=512, m=768, b=128, k=4, dtype=torch.bfloat16, seed=4)
     with torch.no_grad():
         mod.theta_P.normal_(0, 0.02)
         mod.theta_R.normal_(0, 0.02)
     x = torch.randn(64, 512, device="cuda").to(torch.bfloat16)
     with torch.no_grad():
         y0 = mod(x).float().cpu().numpy().astype(np.float64)
-        perm_before = mod._layer.perm_P.clone()
+        perm_before = mod.perm_P.clone()
         mod.end_inner_loop()
         assert float(mod.theta_P.abs().max()) == 0.0 and float(mod.theta_R.abs().max()) == 0.0
-        assert not torch.equal(perm_before, mod._layer.perm_P)
+        assert not torch.equal(perm_before, mod.perm_P)
         y1 = mod(x).float().cpu().numpy().astype(np.float64)
-    err = O.rel_fro(y1, y0)
-    say(f"  function change {err:.2e}")
-    assert err <= TOL["bf16"]
+    check_close("y after the merge", y1, y0, TOL["bf16"], rows=True, cols=True, log=say)
 
 
 # ------------------------------------------------------------------ POET-XQ
@@ -422,7 +402,7 @@ def _xq_layer(cfg, d, T):
              to_dev(d["perm_P"]), to_dev(d["perm_R"]))
     L.step(to_dev(d["x"]), to_dev(d["dy"]))
     torch.cuda.synchronize()
-    return L, I.dequantized(q, sc)
+    return L, O.dequant_rows(q, sc)
 
 
 @pytest.mark.parametrize("name,T", [("mid", 200), ("square", 96), ("mlp13b", 40)])
@@ -437,12 +417,7 @@ def test_xq_layer_parity_small_T(name, T):
                            d["perm_R"], cfg.b, cfg.k)
     g = O.layer_bwd(d["x64"], d["dy64"], W0q, d["theta_P64"], d["theta_R64"], d["perm_P"],
                     d["perm_R"], cfg.b, cfg.k)
-    errs = {"y": O.rel_fro(to_f64(L.y), y_ref), "dx": O.rel_fro(to_f64(L.dx), g["dx"]),
-            "dtheta_P": O.rel_fro(to_f64(L.dtheta_P), g["dtheta_P"]),
-            "dtheta_R": O.rel_fro(to_f64(L.dtheta_R), g["dtheta_R"])}
-    say("  " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
-    for k, v in errs.items():
-        assert v <= TOL[cfg.dtype], (k, v)
+    check_layer(layer_out(L), dict(g, y=y_ref), TOL[cfg.dtype], log=say)
 
 
 def test_xq_layer_full_size():
@@ -453,10 +428,12 @@ def test_xq_layer_full_size():
     G_P = O.cnp_fwd(d["theta_P64"], cfg.b, cfg.k)
     G_R = O.cnp_fwd(d["theta_R64"], cfg.b, cfg.k)
     W = O.weight(W0q, G_R, G_P, d["perm_R"], d["perm_P"])
-    e_y = O.rel_fro(to_f64(L.y[torch.as_tensor(rows, device="cuda")]), d["x64"][rows] @ W.T)
-    e_dx = O.rel_fro(to_f64(L.dx[torch.as_tensor(rows, device="cuda")]), d["dy64"][rows] @ W)
-    say(f"  xq full: y rows {e_y:.2e}  dx rows {e_dx:.2e}")
-    assert e_y <= TOL["bf16"] and e_dx <= TOL["bf16"]
+    ref = {"y": d["x64"][rows] @ W.T, "dx": d["dy64"][rows] @ W}
+    del W
+    g = O.layer_bwd(d["x64"], d["dy64"], W0q, d["theta_P64"], d["theta_R64"], d["perm_P"],
+                    d["perm_R"], cfg.b, cfg.k)
+    ref.update({nm: g[nm] for nm in ("dG_P", "dG_R", "dtheta_P", "dtheta_R")})
+    check_layer(layer_out(L, rows), ref, TOL["bf16"], log=say)
 
 
 def test_graph_replays_match_eager():
@@ -492,7 +469,7 @@ def test_graph_replays_match_eager():
 def test_autograd_module_matches_layer():
     from orthogonal_reparameterized_02_amd.layer import POETXLinear
     torch.manual_seed(0)
-    mod = POETXLinear(n=512, m=768, b=128, k=4, T=64, dtype=torch.bfloat16, seed=3)
+    mod = POETXLinear(n=512, m=768, b=128, k=4, dtype=torch.bfloat16, seed=3)
     with torch.no_grad():
         mod.theta_P.normal_(0, 0.01)
         mod.theta_R.normal_(0, 0.01)
@@ -501,13 +478,49 @@ def test_autograd_module_matches_layer():
     dy = torch.randn_like(y)
     y.backward(dy)
     torch.cuda.synchronize()
-    L = mod._layer
+    pP, pR = mod.perm_P.cpu().numpy(), mod.perm_R.cpu().numpy()
     W0 = to_f64(mod.W0)
-    ref_y, _ = O.layer_fwd(to_f64(x), W0, to_f64(mod.theta_P), to_f64(mod.theta_R),
-                           L.perm_P.cpu().numpy(), L.perm_R.cpu().numpy(), 128, 4)
-    g = O.layer_bwd(to_f64(x), to_f64(dy), W0, to_f64(mod.theta_P), to_f64(mod.theta_R),
-                    L.perm_P.cpu().numpy(), L.perm_R.cpu().numpy(), 128, 4)
-    assert O.rel_fro(to_f64(y), ref_y) <= TOL["bf16"]
-    assert O.rel_fro(to_f64(x.grad), g["dx"]) <= TOL["bf16"]
-    assert O.rel_fro(to_f64(mod.theta_P.grad), g["dtheta_P"]) <= TOL["bf16"]
-    assert O.rel_fro(to_f64(mod.theta_R.grad), g["dtheta_R"]) <= TOL["bf16"]
+    ref_y, _ = O.layer_fwd(to_f64(x), W0, to_f64(mod.theta_P), to_f64(mod.theta_R), pP, pR, 128, 4)
+    g = O.layer_bwd(to_f64(x), to_f64(dy), W0, to_f64(mod.theta_P), to_f64(mod.theta_R), pP, pR,
+                    128, 4)
+    check_layer({"y": to_f64(y), "dx": to_f64(x.grad), "dtheta_P": to_f64(mod.theta_P.grad),
+                 "dtheta_R": to_f64(mod.theta_R.grad)}, dict(g, y=ref_y), TOL["bf16"], log=say)
+
+
+def test_autograd_module_is_reentrant():
+    """Two forwards of different token counts (one with a leading batch
+    axis), both before either backward, then one backward over both: y, dx
+    of each call against the oracle, and the theta gradients against the
+    oracle's over all tokens of both calls (dG sums over tokens and dtheta
+    is linear in dG, so the two calls' gradients add)."""
+    from orthogonal_reparameterized_02_amd.layer import POETXLinear
+    torch.manual_seed(2)
+    mod = POETXLinear(n=512, m=768, b=128, k=4, dtype=torch.bfloat16, seed=5)
+    with torch.no_grad():
+        mod.theta_P.normal_(0, 0.01)
+        mod.theta_R.normal_(0, 0.01)
+    x1 = torch.randn(2, 40, 512, device="cuda").to(torch.bfloat16).requires_grad_(True)
+    x2 = torch.randn(72, 512, device="cuda").to(torch.bfloat16).requires_grad_(True)
+    y1 = mod(x1)
+    y2 = mod(x2)
+    assert y1.shape == (2, 40, 768) and y2.shape == (72, 768)
+    dy1, dy2 = torch.randn_like(y1), torch.randn_like(y2)
+    torch.autograd.backward([y1, y2], [dy1, dy2])
+    torch.cuda.synchronize()
+    pP, pR = mod.perm_P.cpu().numpy(), mod.perm_R.cpu().numpy()
+    W0, thP, thR = to_f64(mod.W0), to_f64(mod.theta_P), to_f64(mod.theta_R)
+    xs = [to_f64(x1).reshape(80, 512), to_f64(x2)]
+    dys = [to_f64(dy1).reshape(80, 768), to_f64(dy2)]
+    for xx, dd, y, gx in ((xs[0], dys[0], y1, x1.grad), (xs[1], dys[1], y2, x2.grad)):
+        ref_y, _ = O.layer_fwd(xx, W0, thP, thR, pP, pR, 128, 4)
+        g = O.layer_bwd(xx, dd, W0, thP, thR, pP, pR, 128, 4)
+        check_layer({"y": to_f64(y).reshape(xx.shape[0], 768),
+                     "dx": to_f64(gx).reshape(xx.shape[0], 512)},
+                    dict(g, y=ref_y), TOL["bf16"], log=say)
+    g = O.layer_bwd(np.concatenate(xs), np.concatenate(dys), W0, thP, thR, pP, pR, 128, 4)
+    check_layer({"dtheta_P": to_f64(mod.theta_P.grad), "dtheta_R": to_f64(mod.theta_R.grad)},
+                g, TOL["bf16"], log=say)
+    with pytest.raises(ValueError, match="features"):
+        mod(torch.zeros(4, 256, dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="dtype"):
+        mod(torch.zeros(4, 512, dtype=torch.float32, device="cuda"))

@@ -290,5 +290,95 @@ def test_int8_base_weight_helper():
     q, s = I.quantize_rows_int8(w)
     assert q.dtype == np.int8 and s.dtype == np.float32
     assert np.abs(q).max() == 127 and q.min() >= -127
-    err = np.abs(I.dequantized(q, s) - w)
+    err = np.abs(O.dequant_rows(q, s) - w)
     assert np.all(err <= s.astype(np.float64)[:, None] / 2 * (1 + 1e-6))
+
+
+def test_dequant_rows_hand_values():
+    """W0[i, j] = s[i] q[i, j]: scales follow output rows (a column-scaled
+    slip gives [[0.5, -0.5], [63.5, 0]])."""
+    q = np.array([[1, -2], [127, 0]], dtype=np.int8)
+    s = np.array([0.5, 0.25], dtype=np.float32)
+    np.testing.assert_array_equal(O.dequant_rows(q, s), [[0.5, -1.0], [31.75, 0.0]])
+
+
+# ---------------------------------------------------------------- comparison metrics
+def test_rel_fro_hand_values():
+    """||got - ref||_F / ||ref||_F against values worked out by hand; the
+    plausible slips (dividing by ||got||, dropping the square roots) give
+    other numbers."""
+    ref = np.array([[1.0, 2.0], [3.0, 5.0]])     # ||ref||^2 = 1 + 4 + 9 + 25 = 39
+    got = np.array([[1.0, 2.0], [3.0, 4.0]])     # one entry off by 1
+    assert O.rel_fro(got, ref) == pytest.approx(1 / np.sqrt(39), rel=1e-15)
+    assert O.rel_fro(got, ref) != pytest.approx(1 / np.sqrt(30), rel=1e-3)   # / ||got||
+    assert O.rel_fro(got, ref) != pytest.approx(1 / 39, rel=1e-3)             # no roots
+    # differences (3, 4): ||diff|| = 5 against ||(6, 8)|| = 10 (||got|| = 15)
+    assert O.rel_fro(np.array([9.0, 12.0]), np.array([6.0, 8.0])) == pytest.approx(0.5, rel=1e-15)
+    assert O.rel_fro(ref, ref) == 0.0
+    assert O.rel_fro(np.array([3.0, 4.0]), np.zeros(2)) == pytest.approx(5.0, rel=1e-15)
+    with pytest.raises(AssertionError):
+        O.rel_fro(np.zeros(3), np.zeros(4))
+
+
+def test_max_ratio_hand_values():
+    """max |got - ref| / max |ref|: differences (0.5, 0, 0, -3) against the
+    largest |ref| = 8 give 3/8 (without the absolute values: 0.5/4; as the
+    largest elementwise ratio: 3/4)."""
+    ref = np.array([[1.0, -8.0], [2.0, 4.0]])
+    got = np.array([[1.5, -8.0], [2.0, 1.0]])
+    assert O.max_ratio(got, ref) == pytest.approx(3 / 8, rel=1e-15)
+    assert O.max_ratio(ref, ref) == 0.0
+    assert O.max_ratio(np.array([0.0, -2.0]), np.zeros(2)) == 2.0
+    assert O.max_ratio(np.zeros((0, 3)), np.zeros((0, 3))) == 0.0
+
+
+def test_rel_fro_slices_hand_values():
+    """One figure per row (axis 0) or per column (axis 1), and per block of
+    a [N, b, b] tensor."""
+    ref = np.array([[3.0, 4.0], [1.0, 0.0], [0.0, 2.0]])
+    got = np.array([[3.0, 4.0], [1.0, 1.0], [0.0, 1.0]])
+    np.testing.assert_allclose(O.rel_fro_slices(got, ref, 0), [0.0, 1.0, 0.5], rtol=1e-15)
+    # columns: (3, 1, 0) exact; (4, 0, 2) against (4, 1, 1): sqrt(2) / sqrt(20)
+    np.testing.assert_allclose(O.rel_fro_slices(got, ref, 1), [0.0, np.sqrt(0.1)], rtol=1e-15)
+    blocks = np.stack([np.eye(2), 2 * np.eye(2)])
+    bad = blocks.copy()
+    bad[1, 0, 1] = 2.0                            # ||diff|| = 2 against ||2 I|| = 2 sqrt(2)
+    np.testing.assert_allclose(O.rel_fro_slices(bad, blocks, 0), [0.0, 1 / np.sqrt(2)], rtol=1e-15)
+
+
+def test_localized_error_needs_the_local_bounds():
+    """Why the parity checks bound more than one norm per tensor: one block
+    of sixteen 5% wrong, or one whole output column of 4096 wrong, stays
+    under a 2e-2 whole-tensor bound but not under the per-block bound or
+    the largest-difference ratio."""
+    rng = np.random.default_rng(0)
+    ref = rng.standard_normal((16, 64, 64))
+    got = ref.copy()
+    got[3] *= 1.05
+    assert O.rel_fro(got, ref) < 2e-2
+    assert O.rel_fro_slices(got, ref, 0).max() == pytest.approx(0.05, rel=1e-12)
+    y = rng.standard_normal((64, 4096))
+    yb = y.copy()
+    yb[:, 17] = 0.0                               # one column lost
+    assert O.rel_fro(yb, y) < 2e-2
+    assert O.max_ratio(yb, y) > 0.1
+    assert O.rel_fro_slices(yb, y, 1).max() > 0.5
+
+
+def test_dG_probes_match_the_full_gradient(rng):
+    """The bilinear probes u^T dG v, pulled back to x and dy, equal the
+    probes of the dG that layer_bwd forms (itself pinned by finite
+    differences), block by block."""
+    L = tiny_layer(rng, m=12, n=16, b=4, k=3, T=9)
+    g = O.layer_bwd(L["x"], L["dy"], L["W0"], L["theta_P"], L["theta_R"], L["perm_P"],
+                    L["perm_R"], 4, 3)
+    G_P, G_R = O.cnp_fwd(L["theta_P"], 4, 3), O.cnp_fwd(L["theta_R"], 4, 3)
+    npr = 3
+    u_P, v_P = rng.standard_normal((2, npr, 4, 4))
+    u_R, v_R = rng.standard_normal((2, npr, 3, 4))
+    pP, pR = O.dG_probes(L["x"], L["dy"], L["W0"], G_P, G_R, L["perm_P"], L["perm_R"],
+                         u_P, v_P, u_R, v_R)
+    np.testing.assert_allclose(pP, np.einsum("qjr,jrc,qjc->qj", u_P, g["dG_P"], v_P), rtol=1e-12,
+                               atol=1e-13)
+    np.testing.assert_allclose(pR, np.einsum("qir,irc,qic->qi", u_R, g["dG_R"], v_R), rtol=1e-12,
+                               atol=1e-13)
