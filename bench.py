@@ -190,11 +190,18 @@ def main() -> int:
     flops = step_flops(cfg)
     peak = PEAK_BF16_TFLOPS if act == P.BF16 else PEAK_FP32_TFLOPS
     tokens_per_s = T / (ms * 1e-3)
-    dense_us = stages["dense_Z"]
-    # b = 256 or 128 in bf16: the dense kernel also forms S = Z G_R^T per block
-    # in its epilogue (the library's fused path), 2 m b flops per token more
-    fused = act == P.BF16 and b in (128, 256) and m % 256 == 0 and n % 64 == 0
-    dense_flops = 2.0 * T * m * n + (2.0 * T * m * b if fused else 0.0)
+    # The roofline covers both dense launches of the step (the forward
+    # Z = V W0f^T and the backward dV = dZ W0f), as the rocprofv3 average of
+    # the kernel does.  b = 256 or 128 in bf16: each also forms its block
+    # product in the epilogue (S = Z G_R^T, dU = dV G_P: 2 m b and 2 n b
+    # flops per token more), where the output width is a multiple of 256.
+    fused_f = act == P.BF16 and b in (128, 256) and m % 256 == 0
+    fused_b = act == P.BF16 and b in (128, 256) and n % 256 == 0
+    fused = fused_f and fused_b
+    flops_pair = (2.0 * T * m * n + (2.0 * T * m * b if fused_f else 0.0)
+                  + 2.0 * T * m * n + (2.0 * T * n * b if fused_b else 0.0))
+    dense_us = (stages["dense_Z"] + stages["dense_dV"]) / 2
+    dense_flops = flops_pair / 2
     dense_tflops = dense_flops / (dense_us * 1e-6) / 1e12
     nblocks = cfg.n_P + cfg.n_R
 
@@ -223,8 +230,11 @@ def main() -> int:
                              "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
         "inner_loop_merge_us": round(merge_us, 2),
-        "roofline": {"kernel": (f"k_nt4<{1 if b == 256 else 2}>: Z = V W0f^T with S = Z G_R^T "
-                                "in the epilogue" if fused else f"{unfused_dense_kernel(T, m)}: Z = V W0f^T"),
+        "roofline": {"kernel": (f"k_nt4<{1 if b == 256 else 2}>, both launches of the step: "
+                                "Z = V W0f^T with S = Z G_R^T and dV = dZ W0f with dU = dV G_P "
+                                "in the epilogue" if fused else
+                                f"{unfused_dense_kernel(T, m)}, both launches of the step: "
+                                "Z = V W0f^T and dV = dZ W0f"),
                      "bound": "mfma", "achieved": dense_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": dense_tflops / peak,
                      "traffic": measured_traffic(cfg.name) if fused else None,

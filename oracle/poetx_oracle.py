@@ -383,8 +383,11 @@ def rel_fro_slices(got: np.ndarray, ref: np.ndarray, axis: int = 0) -> np.ndarra
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
-    return np.array([rel_fro(got.take(i, axis), ref.take(i, axis))
-                     for i in range(got.shape[axis])])
+    rest = tuple(a for a in range(got.ndim) if a != axis)   # summed within each slice
+    diff = got - ref
+    num = np.sqrt(np.sum(diff * diff, axis=rest))
+    den = np.sqrt(np.sum(ref * ref, axis=rest))
+    return num / np.where(den > 0, den, 1.0)
 
 
 # --------------------------------------------------------------------------
