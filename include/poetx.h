@@ -41,7 +41,8 @@
  *   - Arguments are validated on the host before anything is enqueued; on
  *     any error nothing is written.  Permutations being valid is a
  *     precondition that is not checked on the device.
- *   - Entry points are thread-safe and keep no state between calls.
+ *   - Entry points are thread-safe and keep no state between calls, except
+ *     poetx_cnp_fwd_noalloc, whose scratch array is shared by its calls.
  *   - poetx_last_error() returns a message for the calling thread's most
  *     recent failure.
  */
@@ -105,6 +106,28 @@ const char* poetx_last_error(void);
 int32_t poetx_cnp_fwd(int32_t nblk, int32_t b, int32_t k, const float* theta,
                       void* G, void* GT, int32_t g_dtype, void* ws,
                       size_t ws_bytes, poetx_stream_t stream);
+
+/*
+ * poetx_cnp_fwd_noalloc -- poetx_cnp_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same kernels, bitwise the same G and GT.  The unpacked Q
+ * that poetx_cnp_fwd keeps in its workspace goes instead to a library-owned
+ * device array of POETX_NOALLOC_SCRATCH_BYTES bytes, one per GPU, which
+ * exists from the library's load on that GPU until the process ends; the
+ * call itself allocates nothing.  It needs nblk*b*b*2 bytes for bf16 blocks
+ * of 64..512 (e.g. up to 64 blocks of 512 or 256 of 256) and none
+ * otherwise; more gives ERR_WORKSPACE with nothing enqueued.  Every call on
+ * a GPU shares that GPU's array, and each call overwrites what it reads
+ * before reading it (nothing needs clearing), so calls that overlap on one
+ * GPU -- on different streams, or from different threads -- race and give
+ * wrong G.  The array is the one of the calling thread's current device;
+ * `stream` must belong to that device.
+ * Errors as poetx_cnp_fwd (ERR_WORKSPACE: the blocks exceed the array).
+ */
+#define POETX_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t poetx_cnp_fwd_noalloc(int32_t nblk, int32_t b, int32_t k, const float* theta,
+                              void* G, void* GT, int32_t g_dtype, poetx_stream_t stream);
 
 /*
  * poetx_cnp_bwd -- gradient of the packed parameters (technical summary 2.4:

@@ -22,6 +22,7 @@ SIGNATURES = {
     "poetx_status_str": (C.c_char_p, [_i]),
     "poetx_last_error": (C.c_char_p, []),
     "poetx_cnp_fwd": (_i, [_i, _i, _i, _p, _p, _p, _i, _p, _sz, _p]),
+    "poetx_cnp_fwd_noalloc": (_i, [_i, _i, _i, _p, _p, _p, _i, _p]),
     "poetx_cnp_bwd": (_i, [_i, _i, _i, _p, _p, _p, _i, _i, _p, _sz, _p]),
     "poetx_cnp_bwd_after_fwd": (_i, [_i, _i, _i, _p, _p, _p, _i, _i, _p, _sz, _p]),
     "poetx_cnp_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
@@ -39,6 +40,9 @@ SIGNATURES = {
     "poetx_dequant": (_i, [_i, _i, _p, _p, _i, _p, _p]),
     "poetx_set_stage_events": (_i, [_p, _i]),
 }
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # POETX_NOALLOC_SCRATCH_BYTES
 
 
 class Shape(C.Structure):

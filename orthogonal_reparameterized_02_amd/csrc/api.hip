@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/poetx.h"
 #include "kernels.h"
 
@@ -393,6 +395,57 @@ int32_t cnp_bwd_impl(const char* fn, int32_t nblk, int32_t b, int32_t k, const f
   return ok();
 }
 
+// dispatch of the CNP forward once the arguments are checked (ws: the
+// unpacked-Q scratch, at least cnp_ws(nblk, b, k, 0, g_dtype) bytes)
+int32_t cnp_fwd_launch(const char* fn, int32_t nblk, int32_t b, int32_t k, const float* theta,
+                       void* G, void* GT, int32_t g_dtype, void* ws, hipStream_t s) {
+  hipError_t e;
+  if (cnp_uses_panel(b, g_dtype))
+    e = launch_cnp_panel_fwd(nblk, b, k, theta, (bf16*)G, (bf16*)GT, (bf16*)ws, s);
+  else if (g_dtype == POETX_F32)
+    e = launch_cnp_small_fwd<float>(nblk, b, k, theta, (float*)G, (float*)GT, s);
+  else
+    e = launch_cnp_small_fwd<bf16>(nblk, b, k, theta, (bf16*)G, (bf16*)GT, s);
+  if (e != hipSuccess) return dev_fail(e, fn);
+  return ok();
+}
+
+}  // namespace
+
+// ---- library-owned scratch of poetx_cnp_fwd_noalloc -----------------------
+// One copy per GPU, part of the library's code object: it exists on a device
+// from the library's load there until the process ends.  In host code the
+// name `scratch` stands for a host-side shadow, not device memory, so host
+// code never hands it to a kernel, a memset or a copy: every use goes
+// through the device address hipGetSymbolAddress returns, looked up once per
+// device with that device current.
+static __device__ __align__(256) unsigned char scratch[POETX_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[SCRATCH_MAX_DEVICES] = {};
+
+// the device address of `scratch` on the calling thread's current device
+int32_t scratch_on_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return dev_fail(e, fn);
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(POETX_ERR_DEVICE, "%s: device %d outside 0..%d", fn, dev, SCRATCH_MAX_DEVICES - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return dev_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(POETX_ERR_DEVICE, "%s: no device address for the scratch array", fn);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return POETX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -431,16 +484,27 @@ int32_t poetx_cnp_fwd(int32_t nblk, int32_t b, int32_t k, const float* theta, vo
     NEED_PTR(ws);
     if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   }
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  if (cnp_uses_panel(b, g_dtype))
-    e = launch_cnp_panel_fwd(nblk, b, k, theta, (bf16*)G, (bf16*)GT, (bf16*)ws, s);
-  else if (g_dtype == POETX_F32)
-    e = launch_cnp_small_fwd<float>(nblk, b, k, theta, (float*)G, (float*)GT, s);
-  else
-    e = launch_cnp_small_fwd<bf16>(nblk, b, k, theta, (bf16*)G, (bf16*)GT, s);
-  if (e != hipSuccess) return dev_fail(e, fn);
-  return ok();
+  return cnp_fwd_launch(fn, nblk, b, k, theta, G, GT, g_dtype, ws, (hipStream_t)stream);
+}
+
+int32_t poetx_cnp_fwd_noalloc(int32_t nblk, int32_t b, int32_t k, const float* theta, void* G,
+                              void* GT, int32_t g_dtype, poetx_stream_t stream) {
+  const char* fn = "poetx_cnp_fwd_noalloc";
+  int32_t st = check_cnp_args(fn, nblk, b, k, g_dtype);
+  if (st != POETX_OK) return st;
+  NEED_PTR(theta);
+  NEED_PTR(G);
+  OPT_PTR(GT);
+  const size_t need = cnp_ws(nblk, b, k, 0, g_dtype);
+  if (need > (size_t)POETX_NOALLOC_SCRATCH_BYTES)
+    return fail(POETX_ERR_WORKSPACE, "%s: %zu bytes of scratch needed, the library's array holds %zu",
+                fn, need, (size_t)POETX_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    st = scratch_on_current_device(fn, &ws);
+    if (st != POETX_OK) return st;
+  }
+  return cnp_fwd_launch(fn, nblk, b, k, theta, G, GT, g_dtype, ws, (hipStream_t)stream);
 }
 
 

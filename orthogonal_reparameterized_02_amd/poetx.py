@@ -89,6 +89,18 @@ def poetx_cnp_fwd(theta: torch.Tensor, b: int, k: int, G: torch.Tensor,
         _dev(GT, "GT", G.dtype, nblk * b * b, optional=True), act, wp, wb, _stream(stream)))
 
 
+def poetx_cnp_fwd_noalloc(theta: torch.Tensor, b: int, k: int, G: torch.Tensor,
+                          GT: Optional[torch.Tensor] = None, stream=None) -> None:
+    """poetx_cnp_fwd without a workspace: the library's own per-GPU scratch
+    array holds the unpacked Q (calls that overlap on one GPU race)."""
+    nblk = theta.shape[0]
+    act = act_of(G.dtype)
+    tb = b * (b - 1) // 2
+    check("poetx_cnp_fwd_noalloc", lib().poetx_cnp_fwd_noalloc(
+        nblk, b, k, _dev(theta, "theta", torch.float32, nblk * tb), _dev(G, "G", None, nblk * b * b),
+        _dev(GT, "GT", G.dtype, nblk * b * b, optional=True), act, _stream(stream)))
+
+
 def poetx_cnp_bwd(theta: torch.Tensor, dG: torch.Tensor, b: int, k: int, dtheta: torch.Tensor,
                   prec: int, accumulate: bool = False, ws: Optional[torch.Tensor] = None,
                   stream=None, after_fwd: bool = False) -> None:
