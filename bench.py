@@ -48,6 +48,9 @@ def main() -> int:
                     help="memory-saving mode: keep only U, recompute Z in the backward")
     ap.add_argument("--xq", action="store_true",
                     help="int8 base weight (per-row scales), expanded to bf16 in each pass")
+    ap.add_argument("--keep-w0ft", action="store_true",
+                    help="also keep the folded weight transposed and let the backward's dense "
+                         "product read that copy instead of W0f itself (same results)")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel of each timed step from the host instead of "
                          "replaying one captured HIP graph of the step")
@@ -80,7 +83,8 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
-    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act, xmem=args.xmem, xq=args.xq)
+    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act, xmem=args.xmem, xq=args.xq,
+                   keep_w0ft=args.keep_w0ft)
     if args.xq:
         q, sc = I.quantize_rows_int8(I.make_inputs(cfg, seed=args.seed, want=("W0",))["W064"])
         L.load_q(torch.from_numpy(q).cuda(), torch.from_numpy(sc).cuda(), dev(d["theta_P"]),
@@ -166,17 +170,21 @@ def main() -> int:
     stages["cnp_bwd"] = mean_ms(cnp_ev, 2, 3) * 1e3
 
     # ---- once per inner loop (not part of the step): merge W0 <- R W0 P ----
-    merge_ws = torch.empty(P.poetx_workspace_bytes(L.sh, 4), dtype=torch.uint8, device="cuda")
-    merged = torch.empty(cfg.m, cfg.n, dtype=L.dtype, device="cuda")
-    mev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for i in range(6):
-        if i == 1:
-            mev[0].record(stream)
-        P.poetx_merge(L.sh, L.W0f, L.G_R, L.GT_P, L.perm_R_inv, L.perm_P_inv, merged, merge_ws)
-    mev[1].record(stream)
-    torch.cuda.synchronize()
-    merge_us = mev[0].elapsed_time(mev[1]) / 5 * 1e3
-    del merge_ws, merged
+    # (an int8 base weight has no bf16 copy to merge into)
+    merge_us = None
+    if not args.xq:
+        merge_ws = torch.empty(P.poetx_workspace_bytes(L.sh, 4), dtype=torch.uint8, device="cuda")
+        merged = torch.empty(cfg.m, cfg.n, dtype=L.dtype, device="cuda")
+        mev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        for i in range(6):
+            if i == 1:
+                mev[0].record(stream)
+            P.poetx_merge(L.sh, L.W0f, L.G_R, L.GT_P, L.perm_R_inv, L.perm_P_inv, merged,
+                          merge_ws)
+        mev[1].record(stream)
+        torch.cuda.synchronize()
+        merge_us = round(mev[0].elapsed_time(mev[1]) / 5 * 1e3, 2)
+        del merge_ws, merged
 
     if args.copy_probe:
         src = torch.ones(COPY_PROBE_BYTES // 2, dtype=torch.bfloat16, device="cuda")
@@ -222,14 +230,15 @@ def main() -> int:
         "config": {"workload": f"{cfg.name}: POET-X layer m={m} n={n} b={b} k={cfg.k} "
                                f"T={T} tokens, {cfg.dtype} activations/W0, fp32 theta"
                                + (", xmem (Z recomputed in the backward)" if args.xmem else "")
-                               + (", xq (int8 base weight)" if args.xq else ""),
+                               + (", xq (int8 base weight)" if args.xq else "")
+                               + (", W0f kept transposed too" if args.keep_w0ft else ""),
                    "m": m, "n": n, "b": b, "k": cfg.k, "tokens": T, "seed": args.seed},
         "mfma_peak_frac": flops / (ms * 1e-3) / (peak * 1e12),
         "step_tflops": flops / (ms * 1e-3) / 1e12,
         "cnp_blocks_per_s": {"fwd": nblocks / (stages["cnp_fwd"] * 1e-6),
                              "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
-        "inner_loop_merge_us": round(merge_us, 2),
+        "inner_loop_merge_us": merge_us,
         "roofline": {"kernel": (f"k_nt4<{1 if b == 256 else 2}>, both launches of the step: "
                                 "Z = V W0f^T with S = Z G_R^T and dV = dZ W0f with dU = dV G_P "
                                 "in the epilogue" if fused else

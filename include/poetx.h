@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define POETX_ABI_VERSION 1
+#define POETX_ABI_VERSION 2
 
 typedef enum {
   POETX_OK = 0,
@@ -189,10 +189,12 @@ int32_t poetx_fold_perm(int32_t m, int32_t n, int32_t dt, const void* W0,
  * model, INT8, dequantized on the fly when needed; the high-precision weight
  * is never kept).  The base weight is held as int8 q with one fp32 scale per
  * output row: W0[i][j] = s[i] * q[i][j].  poetx_fold_perm folds q
- * (dt = POETX_I8) into q_f and q_fT; poetx_fold_scale folds the scales;
- * poetx_dequant expands the folded weight to bf16 for one layer call.  The
- * bf16 copy lives only in the caller's per-call scratch, so the persistent
- * weight is the int8 one.
+ * (dt = POETX_I8) into q_f and q_fT; poetx_fold_scale folds the scales.
+ * poetx_layer_fwd_q / poetx_layer_bwd_q run the layer on (q_f, q_fT, s_f)
+ * directly: the dense kernel widens the int8 operand to bf16 as it reads it
+ * (exact) and applies s_f to its fp32 sums, so no high-precision copy of the
+ * weight exists at any point.  poetx_dequant (an explicit bf16 copy) remains
+ * for callers that want one.
  *
  * poetx_fold_scale -- s_f[i] = s[perm_R[i]], i < m (fp32).
  * poetx_dequant -- out[r][c] = bf16(scale * q[r][c]) for q int8 [rows][cols]
@@ -205,6 +207,30 @@ int32_t poetx_fold_scale(int32_t m, const float* s, const int32_t* perm_R, float
                          poetx_stream_t stream);
 int32_t poetx_dequant(int32_t rows, int32_t cols, const void* q, const float* scale,
                       int32_t per_row, void* out, poetx_stream_t stream);
+
+/*
+ * poetx_layer_fwd_q / poetx_layer_bwd_q -- poetx_layer_fwd / _bwd (xmem = 0)
+ * or their memory-saving variants (xmem != 0) on an int8 base weight
+ * (technical summary 2.6), with W0f = diag(s_f) q_f in place of the bf16 W0f:
+ *   q_f  [m][n] int8, q_fT [n][m] int8 (poetx_fold_perm with POETX_I8),
+ *   s_f  [m] fp32 (poetx_fold_scale).
+ * The forward forms Z = (V q_f^T) diag(s_f); the backward forms
+ * dZ' = dZ diag(s_f) in the R-side block pass and dV = dZ' q_f.  Every
+ * other argument, and the saved / workspace sizes (which 0..3 as for the
+ * bf16 calls), are those of the bf16 calls.  bwd: G_P and q_f are read only
+ * with xmem (may be NULL otherwise).  Needs bf16 activations, b >= 64 and
+ * m, n multiples of 256 (ERR_UNSUPPORTED otherwise).
+ * Errors: ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE.
+ */
+int32_t poetx_layer_fwd_q(const poetx_shape* sh, const void* x, const void* G_P, const void* G_R,
+                          const int8_t* q_f, const float* s_f, const int32_t* perm_P,
+                          const int32_t* perm_R_inv, void* y, void* saved, void* ws,
+                          size_t ws_bytes, int32_t xmem, poetx_stream_t stream);
+int32_t poetx_layer_bwd_q(const poetx_shape* sh, const void* dy, const void* G_P, const void* GT_P,
+                          const void* GT_R, const int8_t* q_f, const int8_t* q_fT,
+                          const float* s_f, const int32_t* perm_P_inv, const int32_t* perm_R,
+                          const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
+                          size_t ws_bytes, int32_t xmem, poetx_stream_t stream);
 
 /*
  * poetx_layer_fwd -- input-centric forward pass (technical summary 2.1-2.3).
@@ -226,11 +252,20 @@ int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P,
                         void* ws, size_t ws_bytes, poetx_stream_t stream);
 
 /*
- * poetx_layer_bwd -- backward pass.
+ * poetx_layer_bwd -- backward pass ("POET-X ...", technical summary 2.1-2.3:
+ * the same input-centric chain run in reverse, block products batched,
+ * permutations as index maps; 2.5: the default, fast mode keeps the
+ * forward's activations for it; "Reparameterized LLM Training ...",
+ * Abstract: W0 stays fixed, only the orthogonal factors learn).
  *   dy    [T][m]        dL/dy (act)
  *   GT_P  [n/b][b][b]   P-side blocks transposed (act), from poetx_cnp_fwd
  *   GT_R  [m/b][b][b]   R-side blocks transposed (act)
- *   W0fT  [n][m]        folded weight transposed (act)
+ *   W0f   [m][n]        folded weight (act), the forward's own
+ *   W0fT  [n][m]        its transpose (act) or NULL.  With NULL the dense
+ *                       product dV = dZ W0f reads W0f itself (K-major), so
+ *                       the fixed weight is held once; with a transposed
+ *                       copy it reads that.  Both give bitwise the same
+ *                       results.
  *   perm_P_inv [n], perm_R [m]  int32 index maps
  *   saved as written by poetx_layer_fwd for the same shape and inputs
  *   dx    [T][n]        dL/dx (act)
@@ -241,7 +276,7 @@ int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P,
  * Errors: ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE.
  */
 int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P,
-                        const void* GT_R, const void* W0fT,
+                        const void* GT_R, const void* W0f, const void* W0fT,
                         const int32_t* perm_P_inv, const int32_t* perm_R,
                         const void* saved, void* dx, float* dG_P, float* dG_R,
                         void* ws, size_t ws_bytes, poetx_stream_t stream);
@@ -257,9 +292,8 @@ int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P,
  * buffer is T*m*sizeof(act) bytes smaller and the backward does one more
  * dense product (2 T m n flops) and one more block product (2 T n b flops).
  *   fwd: arguments as poetx_layer_fwd; ws poetx_workspace_bytes(sh, 2) bytes.
- *   bwd: arguments as poetx_layer_bwd plus
- *        G_P [n/b][b][b] (act) and W0f [m][n] (act);
- *        ws poetx_workspace_bytes(sh, 3) bytes.
+ *   bwd: arguments as poetx_layer_bwd plus G_P [n/b][b][b] (act) (W0fT
+ *        may be NULL as there); ws poetx_workspace_bytes(sh, 3) bytes.
  * Errors: ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE.
  */
 int32_t poetx_layer_fwd_xmem(const poetx_shape* sh, const void* x, const void* G_P,

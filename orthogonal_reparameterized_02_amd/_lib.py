@@ -28,7 +28,7 @@ SIGNATURES = {
     "poetx_cnp_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "poetx_fold_perm": (_i, [_i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]),
     "poetx_layer_fwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
-    "poetx_layer_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "poetx_layer_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "poetx_workspace_bytes": (_sz, [_p, _i]),
     "poetx_saved_bytes": (_sz, [_p]),
     "poetx_layer_fwd_xmem": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
@@ -36,6 +36,9 @@ SIGNATURES = {
                                   _p]),
     "poetx_saved_bytes_xmem": (_sz, [_p]),
     "poetx_merge": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "poetx_layer_fwd_q": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _i, _p]),
+    "poetx_layer_bwd_q": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz,
+                               _i, _p]),
     "poetx_fold_scale": (_i, [_i, _p, _p, _p, _p]),
     "poetx_dequant": (_i, [_i, _i, _p, _p, _i, _p, _p]),
     "poetx_set_stage_events": (_i, [_p, _i]),
@@ -43,6 +46,7 @@ SIGNATURES = {
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20  # POETX_NOALLOC_SCRATCH_BYTES
+ABI_VERSION = 2                   # POETX_ABI_VERSION
 
 
 class Shape(C.Structure):
@@ -69,7 +73,7 @@ def lib() -> C.CDLL:
         for name, (res, args) in SIGNATURES.items():
             f = getattr(L, name)
             f.restype, f.argtypes = res, args
-        if L.poetx_abi_version() != 1:
+        if L.poetx_abi_version() != ABI_VERSION:
             raise RuntimeError("libpoetx.so ABI version mismatch")
         _lib = L
     return _lib

@@ -162,26 +162,66 @@ template <typename TS> const TS* at(const void* base, size_t off) {
 }
 
 // ---- the layer passes, per storage type ---------------------------------
-// C[bt] = A[bt] B[bt]^T
+// The fixed weight of a layer call: W0f (and W0fT) in the activation type,
+// or an int8 pair q_f / q_fT with one fp32 scale per output row, s_f.
+template <typename TS>
+struct Weight {
+  const TS* f = nullptr;       // W0f  [m][n]
+  const TS* fT = nullptr;      // W0fT [n][m]
+  const int8_t* q = nullptr;   // q_f  [m][n]
+  const int8_t* qT = nullptr;  // q_fT [n][m]
+  const float* s = nullptr;    // s_f  [m]
+  bool quant() const { return s != nullptr; }
+};
+
+// C[bt] = A[bt] B[bt]^T (column c of C[bt] scaled by cscale[bt * sS + c]
+// when cscale is set: MFMA path only)
 template <typename TS>
 hipError_t nt(bool mfma, int batch, int M, int N, int K, const TS* A, long lda, long sA,
-              const TS* B, long ldb, long sB, TS* C, long ldc, long sC, hipStream_t s) {
+              const TS* B, long ldb, long sB, TS* C, long ldc, long sC, hipStream_t s,
+              const float* cscale = nullptr, long sS = 0) {
   if constexpr (sizeof(TS) == 2) {
     if (mfma && mfma_nt_ok(M, N, K))
-      return launch_mfma_nt(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+      return launch_mfma_nt(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s, cscale, sS);
   }
+  if (cscale) return hipErrorInvalidValue;
   return launch_simple_nt<TS>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
 }
 
 // Out[:, jb + n] = sum_k A[:, jb + k] Gb[j][n][k] for every block j (A and
-// Out row pitch `width`): the per-token block products
+// Out row pitch `width`): the per-token block products (output column c
+// scaled by cscale[c] when cscale is set)
 template <typename TS>
 hipError_t blocks(bool mfma, int nblk, int T, int width, int b, const TS* A, const TS* Gb, TS* Out,
-                  hipStream_t s) {
+                  hipStream_t s, const float* cscale = nullptr) {
   if constexpr (sizeof(TS) == 2) {
-    if (mfma && mfma_blocks_ok(b)) return launch_mfma_blocks(nblk, T, width, b, A, Gb, Out, s);
+    if (mfma && mfma_blocks_ok(b))
+      return launch_mfma_blocks(nblk, T, width, b, A, Gb, Out, s, cscale);
   }
-  return nt<TS>(mfma, nblk, T, b, b, A, width, b, Gb, b, (long)b * b, Out, width, b, s);
+  return nt<TS>(mfma, nblk, T, b, b, A, width, b, Gb, b, (long)b * b, Out, width, b, s, cscale, b);
+}
+
+// Z = V W0f^T (T x m), and with the block epilogue (b = 128 or 256, S
+// set) S_i = Z_i G_Ri^T in the same kernel; false from `fused` when the
+// caller must form S itself
+template <typename TS>
+hipError_t dense_fwd(bool mf, const poetx_shape* sh, const TS* V, const Weight<TS>& W, TS* Z,
+                     const TS* G_R, TS* S, bool& fused, hipStream_t s) {
+  const int m = sh->m, n = sh->n, b = sh->b, T = sh->T;
+  fused = false;
+  if constexpr (sizeof(TS) == 2) {
+    if (W.quant()) {
+      fused = S && mfma_nt_block_ok(T, m, n, b);
+      return launch_mfma_nt_q(T, m, n, b, V, n, W.q, n, Z, m, W.s, fused ? G_R : nullptr,
+                              fused ? S : nullptr, m, s);
+    }
+    if (mf && mfma_nt_block_ok(T, m, n, b)) {
+      fused = S != nullptr;
+      return launch_mfma_nt_block(T, m, n, b, V, n, W.f, n, Z, m, fused ? G_R : nullptr,
+                                  fused ? S : nullptr, m, s);
+    }
+  }
+  return nt<TS>(mf, 1, T, m, n, V, n, 0, W.f, n, 0, Z, m, 0, s);
 }
 
 // out[bt] = A_bt^T B_bt over T tokens, D x D blocks at column offsets bt*D
@@ -196,7 +236,7 @@ hipError_t tn(bool mfma, int batch, int D, int T, const TS* A, long lda, const T
 
 template <typename TS>
 int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const TS* G_R,
-                       const TS* W0f, const int32_t* perm_P, const int32_t* perm_R_inv, TS* y,
+                       const Weight<TS>& W, const int32_t* perm_P, const int32_t* perm_R_inv, TS* y,
                        void* saved, void* ws, hipStream_t s, bool xmem) {
   const int m = sh->m, n = sh->n, b = sh->b, T = sh->T;
   const int es = (int)sizeof(TS);
@@ -216,25 +256,18 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
   if ((e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
     return dev_fail(e, "P-side blocks");
   mark(2, s);
-  if constexpr (sizeof(TS) == 2) {
-    if (mf && mfma_nt_block_ok(T, m, n, b)) {
-      // Z = V W0f^T and, per output block, S_i = Z_i G_Ri^T in one kernel
-      if ((e = launch_mfma_nt_block(T, m, n, b, V, n, W0f, n, Z, m, G_R, S, m, s)) != hipSuccess)
-        return dev_fail(e, "W0 product + R-side blocks");
-      mark(3, s);
-      mark(4, s);
-      goto scatter;
-    }
+  {
+    // Z = V W0f^T and, where the dense kernel carries the block epilogue,
+    // S_i = Z_i G_Ri^T in the same kernel
+    bool fused = false;
+    if ((e = dense_fwd<TS>(mf, sh, V, W, Z, G_R, S, fused, s)) != hipSuccess)
+      return dev_fail(e, "W0 product");
+    mark(3, s);
+    // S_i = Z_i G_Ri^T
+    if (!fused && (e = blocks<TS>(mf, m / b, T, m, b, Z, G_R, S, s)) != hipSuccess)
+      return dev_fail(e, "R-side blocks");
+    mark(4, s);
   }
-  // Z = V W0f^T
-  if ((e = nt<TS>(mf, 1, T, m, n, V, n, 0, W0f, n, 0, Z, m, 0, s)) != hipSuccess)
-    return dev_fail(e, "W0 product");
-  mark(3, s);
-  // S_i = Z_i G_Ri^T
-  if ((e = blocks<TS>(mf, m / b, T, m, b, Z, G_R, S, s)) != hipSuccess)
-    return dev_fail(e, "R-side blocks");
-  mark(4, s);
-scatter:
   // y[:, pi_R[c]] = S[:, c]  <=>  y = S[:, pi_R^{-1}]
   if ((e = launch_permute_cols(T, m, es, S, perm_R_inv, y, s)) != hipSuccess)
     return dev_fail(e, "scatter y");
@@ -244,9 +277,9 @@ scatter:
 
 template <typename TS>
 int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, const TS* GT_R,
-                       const TS* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
+                       const Weight<TS>& W, const int32_t* perm_P_inv, const int32_t* perm_R,
                        const void* saved, TS* dx, float* dG_P, float* dG_R, void* ws,
-                       hipStream_t s, const TS* G_P = nullptr, const TS* W0f = nullptr) {
+                       hipStream_t s, const TS* G_P = nullptr) {
   const int m = sh->m, n = sh->n, b = sh->b, T = sh->T;
   const int es = (int)sizeof(TS);
   const bool mf = use_mfma(sh);
@@ -268,16 +301,8 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
     TS* Zr = at<TS>(ws, w.Z);
     if ((e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
       return dev_fail(e, "recompute V");
-    bool done = false;
-    if constexpr (sizeof(TS) == 2) {
-      if (mf && mfma_nt_block_ok(T, m, n, b)) {
-        if ((e = launch_mfma_nt_block(T, m, n, b, V, n, W0f, n, Zr, m, nullptr, nullptr, 0, s)) !=
-            hipSuccess)
-          return dev_fail(e, "recompute Z");
-        done = true;
-      }
-    }
-    if (!done && (e = nt<TS>(mf, 1, T, m, n, V, n, 0, W0f, n, 0, Zr, m, 0, s)) != hipSuccess)
+    bool fused = false;
+    if ((e = dense_fwd<TS>(mf, sh, V, W, Zr, nullptr, nullptr, fused, s)) != hipSuccess)
       return dev_fail(e, "recompute Z");
     Z = Zr;
   } else {
@@ -287,8 +312,10 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   // dS = dy[:, pi_R]
   if ((e = launch_permute_cols(T, m, es, dy, perm_R, dS, s)) != hipSuccess) return dev_fail(e, "gather dy");
   mark(1, s);
-  // dZ_i = dS_i G_Ri  (B operand G_Ri^T)
-  if ((e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s)) != hipSuccess)
+  // dZ_i = dS_i G_Ri  (B operand G_Ri^T).  An int8 weight W0f = diag(s_f) q_f
+  // gives dV = dZ W0f = (dZ diag(s_f)) q_f: the scale goes on dZ's columns
+  // here, where it is one multiply per element before rounding.
+  if ((e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s, W.s)) != hipSuccess)
     return dev_fail(e, "R-side blocks (bwd)");
   mark(2, s);
   // dG_Ri = dS_i^T Z_i.  On the MFMA path dG_R waits for dG_P and the two
@@ -301,25 +328,41 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
     return dev_fail(e, "dG_R");
   mark(3, s);
   {
-    bool fused = false;
+    // dV = dZ W0f and, where the dense kernel carries the block epilogue
+    // (b = 128, 256), dU_j = dV_j G_Pj in the same kernel.  The weight is
+    // read as W0fT (N-major) when the caller keeps that copy, else straight
+    // from W0f (K-major): the same products in the same order.
+    bool fused = false, dv_done = false;
     if constexpr (sizeof(TS) == 2) {
-      if (mf && mfma_nt_block_ok(T, n, m, b)) {
-        // dV = dZ W0f and, per input block, dU_j = dV_j G_Pj in one kernel
-        if ((e = launch_mfma_nt_block(T, n, m, b, dZ, m, W0fT, m, dV, n, GT_P, dU, n, s)) != hipSuccess)
+      const bool epi = mfma_nt_block_ok(T, n, m, b);
+      if (W.quant()) {
+        // dV = dZ' q_f (B operand q_fT)
+        fused = epi;
+        if ((e = launch_mfma_nt_q(T, n, m, b, dZ, m, W.qT, m, dV, n, nullptr,
+                                  fused ? GT_P : nullptr, fused ? dU : nullptr, n, s)) != hipSuccess)
+          return dev_fail(e, "W0 product (bwd)");
+        dv_done = true;
+      } else if (mf && W.fT && epi) {
+        if ((e = launch_mfma_nt_block(T, n, m, b, dZ, m, W.fT, m, dV, n, GT_P, dU, n, s)) != hipSuccess)
           return dev_fail(e, "W0 product + P-side blocks (bwd)");
-        mark(4, s);
-        fused = true;
+        fused = dv_done = true;
+      } else if (mf && !W.fT && mfma_nt_kmajor_ok(T, n, m, m, n, n)) {
+        fused = epi;
+        if ((e = launch_mfma_nt_kmajor(T, n, m, b, dZ, m, W.f, n, dV, n, fused ? GT_P : nullptr,
+                                       fused ? dU : nullptr, n, s)) != hipSuccess)
+          return dev_fail(e, "W0 product (bwd)");
+        dv_done = true;
       }
     }
-    if (!fused) {
-      // dV = dZ W0f  (B operand W0f^T)
-      if ((e = nt<TS>(mf, 1, T, n, m, dZ, m, 0, W0fT, m, 0, dV, n, 0, s)) != hipSuccess)
-        return dev_fail(e, "W0 product (bwd)");
-      mark(4, s);
-      // dU_j = dV_j G_Pj
-      if ((e = blocks<TS>(mf, n / b, T, n, b, dV, GT_P, dU, s)) != hipSuccess)
-        return dev_fail(e, "P-side blocks (bwd)");
+    if (!dv_done) {
+      e = W.fT ? nt<TS>(mf, 1, T, n, m, dZ, m, 0, W.fT, m, 0, dV, n, 0, s)
+               : launch_simple_nt<TS>(1, T, n, m, dZ, m, 0, W.f, n, 0, dV, n, 0, s, true);
+      if (e != hipSuccess) return dev_fail(e, "W0 product (bwd)");
     }
+    mark(4, s);
+    // dU_j = dV_j G_Pj
+    if (!fused && (e = blocks<TS>(mf, n / b, T, n, b, dV, GT_P, dU, s)) != hipSuccess)
+      return dev_fail(e, "P-side blocks (bwd)");
   }
   mark(5, s);
   // dG_Pj = dV_j^T U_j
@@ -591,16 +634,37 @@ size_t poetx_saved_bytes_xmem(const poetx_shape* sh) {
   return saved_total(sh, true);
 }
 
+// an int8 weight runs on the MFMA path, whose dense kernel needs both
+// widths to be whole 256-column tiles
+static int32_t check_quant(const char* fn, const poetx_shape* sh) {
+  if (sh->act != POETX_BF16)
+    return fail(POETX_ERR_UNSUPPORTED, "%s: an int8 weight needs bf16 activations", fn);
+  if (sh->b < 64 || sh->m % 256 || sh->n % 256 || sh->m >= (1 << 21) || sh->n >= (1 << 21))
+    return fail(POETX_ERR_UNSUPPORTED,
+                "%s: an int8 weight needs b >= 64 and m, n multiples of 256 below 2^21 "
+                "(m=%d n=%d b=%d)", fn, sh->m, sh->n, sh->b);
+  return POETX_OK;
+}
+
+// W0f set: the activation-type weight; s_f set: the int8 pair (q_f, s_f)
 static int32_t layer_fwd_entry(const char* fn, bool xmem, const poetx_shape* sh, const void* x,
                                const void* G_P, const void* G_R, const void* W0f,
-                               const int32_t* perm_P, const int32_t* perm_R_inv, void* y,
-                               void* saved, void* ws, size_t ws_bytes, poetx_stream_t stream) {
+                               const int8_t* q_f, const float* s_f, const int32_t* perm_P,
+                               const int32_t* perm_R_inv, void* y, void* saved, void* ws,
+                               size_t ws_bytes, poetx_stream_t stream) {
   int32_t st = check_shape(fn, sh);
   if (st != POETX_OK) return st;
+  const bool quant = s_f != nullptr || q_f != nullptr;
+  if (quant && (st = check_quant(fn, sh)) != POETX_OK) return st;
   NEED_PTR(x);
   NEED_PTR(G_P);
   NEED_PTR(G_R);
-  NEED_PTR(W0f);
+  if (quant) {
+    NEED_PTR(q_f);
+    NEED_PTR(s_f);
+  } else {
+    NEED_PTR(W0f);
+  }
   NEED_PTR(perm_P);
   NEED_PTR(perm_R_inv);
   NEED_PTR(y);
@@ -609,44 +673,70 @@ static int32_t layer_fwd_entry(const char* fn, bool xmem, const poetx_shape* sh,
   const size_t need = fwd_ws(sh, xmem).total;
   if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
-  if (sh->act == POETX_BF16)
-    return layer_fwd_impl<bf16>(sh, (const bf16*)x, (const bf16*)G_P, (const bf16*)G_R,
-                                (const bf16*)W0f, perm_P, perm_R_inv, (bf16*)y, saved, ws, s, xmem);
-  return layer_fwd_impl<float>(sh, (const float*)x, (const float*)G_P, (const float*)G_R,
-                               (const float*)W0f, perm_P, perm_R_inv, (float*)y, saved, ws, s,
-                               xmem);
+  if (sh->act == POETX_BF16) {
+    Weight<bf16> W;
+    W.f = (const bf16*)W0f;
+    W.q = q_f;
+    W.s = s_f;
+    return layer_fwd_impl<bf16>(sh, (const bf16*)x, (const bf16*)G_P, (const bf16*)G_R, W, perm_P,
+                                perm_R_inv, (bf16*)y, saved, ws, s, xmem);
+  }
+  Weight<float> W;
+  W.f = (const float*)W0f;
+  return layer_fwd_impl<float>(sh, (const float*)x, (const float*)G_P, (const float*)G_R, W,
+                               perm_P, perm_R_inv, (float*)y, saved, ws, s, xmem);
 }
 
 int32_t poetx_layer_fwd(const poetx_shape* sh, const void* x, const void* G_P, const void* G_R,
                         const void* W0f, const int32_t* perm_P, const int32_t* perm_R_inv,
                         void* y, void* saved, void* ws, size_t ws_bytes, poetx_stream_t stream) {
-  return layer_fwd_entry("poetx_layer_fwd", false, sh, x, G_P, G_R, W0f, perm_P, perm_R_inv, y,
-                         saved, ws, ws_bytes, stream);
+  return layer_fwd_entry("poetx_layer_fwd", false, sh, x, G_P, G_R, W0f, nullptr, nullptr, perm_P,
+                         perm_R_inv, y, saved, ws, ws_bytes, stream);
 }
 
 int32_t poetx_layer_fwd_xmem(const poetx_shape* sh, const void* x, const void* G_P,
                              const void* G_R, const void* W0f, const int32_t* perm_P,
                              const int32_t* perm_R_inv, void* y, void* saved, void* ws,
                              size_t ws_bytes, poetx_stream_t stream) {
-  return layer_fwd_entry("poetx_layer_fwd_xmem", true, sh, x, G_P, G_R, W0f, perm_P, perm_R_inv,
-                         y, saved, ws, ws_bytes, stream);
+  return layer_fwd_entry("poetx_layer_fwd_xmem", true, sh, x, G_P, G_R, W0f, nullptr, nullptr,
+                         perm_P, perm_R_inv, y, saved, ws, ws_bytes, stream);
 }
 
+int32_t poetx_layer_fwd_q(const poetx_shape* sh, const void* x, const void* G_P, const void* G_R,
+                          const int8_t* q_f, const float* s_f, const int32_t* perm_P,
+                          const int32_t* perm_R_inv, void* y, void* saved, void* ws,
+                          size_t ws_bytes, int32_t xmem, poetx_stream_t stream) {
+  if (!s_f) return fail(POETX_ERR_ARG, "poetx_layer_fwd_q: null pointer 's_f'");
+  return layer_fwd_entry("poetx_layer_fwd_q", xmem != 0, sh, x, G_P, G_R, nullptr, q_f, s_f,
+                         perm_P, perm_R_inv, y, saved, ws, ws_bytes, stream);
+}
+
+// W0f / W0fT set: the activation-type weight; s_f set: the int8 pair
+// (q_f, q_fT, s_f); G_P and W0f / q_f only for the memory-saving mode
 static int32_t layer_bwd_entry(const char* fn, bool xmem, const poetx_shape* sh, const void* dy,
                                const void* G_P, const void* GT_P, const void* GT_R,
-                               const void* W0f, const void* W0fT, const int32_t* perm_P_inv,
+                               const void* W0f, const void* W0fT, const int8_t* q_f,
+                               const int8_t* q_fT, const float* s_f, const int32_t* perm_P_inv,
                                const int32_t* perm_R, const void* saved, void* dx, float* dG_P,
                                float* dG_R, void* ws, size_t ws_bytes, poetx_stream_t stream) {
   int32_t st = check_shape(fn, sh);
   if (st != POETX_OK) return st;
+  const bool quant = s_f != nullptr;
+  if (quant && (st = check_quant(fn, sh)) != POETX_OK) return st;
   NEED_PTR(dy);
   if (xmem) {
     NEED_PTR(G_P);
-    NEED_PTR(W0f);
+    if (quant) NEED_PTR(q_f);
   }
   NEED_PTR(GT_P);
   NEED_PTR(GT_R);
-  NEED_PTR(W0fT);
+  if (quant) {
+    NEED_PTR(q_fT);
+    NEED_PTR(s_f);
+  } else {
+    NEED_PTR(W0f);
+    OPT_PTR(W0fT);
+  }
   NEED_PTR(perm_P_inv);
   NEED_PTR(perm_R);
   NEED_PTR(saved);
@@ -657,23 +747,32 @@ static int32_t layer_bwd_entry(const char* fn, bool xmem, const poetx_shape* sh,
   const size_t need = bwd_ws(sh, xmem).total;
   if (ws_bytes < need) return fail(POETX_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
   hipStream_t s = (hipStream_t)stream;
-  if (sh->act == POETX_BF16)
-    return layer_bwd_impl<bf16>(sh, (const bf16*)dy, (const bf16*)GT_P, (const bf16*)GT_R,
-                                (const bf16*)W0fT, perm_P_inv, perm_R, saved, (bf16*)dx, dG_P,
-                                dG_R, ws, s, xmem ? (const bf16*)G_P : nullptr,
-                                (const bf16*)W0f);
-  return layer_bwd_impl<float>(sh, (const float*)dy, (const float*)GT_P, (const float*)GT_R,
-                               (const float*)W0fT, perm_P_inv, perm_R, saved, (float*)dx, dG_P,
-                               dG_R, ws, s, xmem ? (const float*)G_P : nullptr,
-                               (const float*)W0f);
+  if (sh->act == POETX_BF16) {
+    Weight<bf16> W;
+    W.f = (const bf16*)W0f;
+    W.fT = (const bf16*)W0fT;
+    W.q = q_f;
+    W.qT = q_fT;
+    W.s = s_f;
+    return layer_bwd_impl<bf16>(sh, (const bf16*)dy, (const bf16*)GT_P, (const bf16*)GT_R, W,
+                                perm_P_inv, perm_R, saved, (bf16*)dx, dG_P, dG_R, ws, s,
+                                xmem ? (const bf16*)G_P : nullptr);
+  }
+  Weight<float> W;
+  W.f = (const float*)W0f;
+  W.fT = (const float*)W0fT;
+  return layer_bwd_impl<float>(sh, (const float*)dy, (const float*)GT_P, (const float*)GT_R, W,
+                               perm_P_inv, perm_R, saved, (float*)dx, dG_P, dG_R, ws, s,
+                               xmem ? (const float*)G_P : nullptr);
 }
 
 int32_t poetx_layer_bwd(const poetx_shape* sh, const void* dy, const void* GT_P, const void* GT_R,
-                        const void* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
-                        const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
-                        size_t ws_bytes, poetx_stream_t stream) {
-  return layer_bwd_entry("poetx_layer_bwd", false, sh, dy, nullptr, GT_P, GT_R, nullptr, W0fT,
-                         perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws, ws_bytes, stream);
+                        const void* W0f, const void* W0fT, const int32_t* perm_P_inv,
+                        const int32_t* perm_R, const void* saved, void* dx, float* dG_P,
+                        float* dG_R, void* ws, size_t ws_bytes, poetx_stream_t stream) {
+  return layer_bwd_entry("poetx_layer_bwd", false, sh, dy, nullptr, GT_P, GT_R, W0f, W0fT,
+                         nullptr, nullptr, nullptr, perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws,
+                         ws_bytes, stream);
 }
 
 int32_t poetx_layer_bwd_xmem(const poetx_shape* sh, const void* dy, const void* G_P,
@@ -681,8 +780,20 @@ int32_t poetx_layer_bwd_xmem(const poetx_shape* sh, const void* dy, const void* 
                              const void* W0fT, const int32_t* perm_P_inv, const int32_t* perm_R,
                              const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
                              size_t ws_bytes, poetx_stream_t stream) {
-  return layer_bwd_entry("poetx_layer_bwd_xmem", true, sh, dy, G_P, GT_P, GT_R, W0f, W0fT,
-                         perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws, ws_bytes, stream);
+  return layer_bwd_entry("poetx_layer_bwd_xmem", true, sh, dy, G_P, GT_P, GT_R, W0f, W0fT, nullptr,
+                         nullptr, nullptr, perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws, ws_bytes,
+                         stream);
+}
+
+int32_t poetx_layer_bwd_q(const poetx_shape* sh, const void* dy, const void* G_P, const void* GT_P,
+                          const void* GT_R, const int8_t* q_f, const int8_t* q_fT,
+                          const float* s_f, const int32_t* perm_P_inv, const int32_t* perm_R,
+                          const void* saved, void* dx, float* dG_P, float* dG_R, void* ws,
+                          size_t ws_bytes, int32_t xmem, poetx_stream_t stream) {
+  if (!s_f) return fail(POETX_ERR_ARG, "poetx_layer_bwd_q: null pointer 's_f'");
+  return layer_bwd_entry("poetx_layer_bwd_q", xmem != 0, sh, dy, G_P, GT_P, GT_R, nullptr, nullptr,
+                         q_f, q_fT, s_f, perm_P_inv, perm_R, saved, dx, dG_P, dG_R, ws, ws_bytes,
+                         stream);
 }
 
 int32_t poetx_merge(const poetx_shape* sh, const void* W0f, const void* G_R, const void* GT_P,

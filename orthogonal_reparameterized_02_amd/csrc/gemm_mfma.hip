@@ -117,9 +117,11 @@ __device__ __forceinline__ void tile_of(int wg, int nwg, int tilesM, int tilesN,
 // multiples of 32, so a fragment's swizzle keys are fixed per lane.  Each
 // lane packs its row pair (r, r+1) of one column; lanes l and l^1 swap
 // halves (DPP quad permute) so each writes two adjacent columns of one row.
-template <int FM, int FN>
-__device__ __forceinline__ void acc_to_slabs(const f32x16_t (&acc)[FM][FN], char* lds, int slab_bytes,
-                                             int rbase, int cbase, int lane, int r_lo, int r_hi) {
+// With SC, column c of the tile is scaled by cs[c] (fp32, before rounding).
+template <int FM, int FN, bool SC>
+__device__ __forceinline__ void acc_to_slabs_impl(const f32x16_t (&acc)[FM][FN], char* lds,
+                                                  int slab_bytes, int rbase, int cbase, int lane,
+                                                  int r_lo, int r_hi, const float* __restrict__ cs) {
   const int odd = lane & 1;
   const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
   const int rl = 4 * (lane >> 5) + odd;  // row within an 8-row group for r % 4 == 0
@@ -133,9 +135,11 @@ __device__ __forceinline__ void acc_to_slabs(const f32x16_t (&acc)[FM][FN], char
       const int col = cbase + j * 32 + cl;
       char* base = lds + (col >> 6) * slab_bytes + (fr + rl) * ROWB + (col & 7) * 2;
       const int chx = ((col >> 3) & 7) ^ ((fr >> 3) & 4);
+      const float sc = SC ? cs[cbase + j * 32 + (lane & 31)] : 1.0f;  // this lane's column
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const uint32_t p = pack2bf(acc[i][j][r], acc[i][j][r + 1]);
+        const uint32_t p = SC ? pack2bf(acc[i][j][r] * sc, acc[i][j][r + 1] * sc)
+                              : pack2bf(acc[i][j][r], acc[i][j][r + 1]);
         const uint32_t q = (uint32_t)__builtin_amdgcn_mov_dpp((int)p, 0xB1, 0xF, 0xF, true);
         const uint32_t v = __builtin_amdgcn_perm(q, p, sel);
         const int key = chx ^ ((r & 3) + rl) ^ (r >> 2);
@@ -143,6 +147,16 @@ __device__ __forceinline__ void acc_to_slabs(const f32x16_t (&acc)[FM][FN], char
       }
     }
   }
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void acc_to_slabs(const f32x16_t (&acc)[FM][FN], char* lds, int slab_bytes,
+                                             int rbase, int cbase, int lane, int r_lo, int r_hi,
+                                             const float* __restrict__ cs = nullptr) {
+  if (cs)
+    acc_to_slabs_impl<FM, FN, true>(acc, lds, slab_bytes, rbase, cbase, lane, r_lo, r_hi, cs);
+  else
+    acc_to_slabs_impl<FM, FN, false>(acc, lds, slab_bytes, rbase, cbase, lane, r_lo, r_hi, cs);
 }
 
 // Copy ROWS x COLS bf16 from the slab layout to global memory with 16-byte
@@ -168,10 +182,34 @@ __device__ __forceinline__ void slabs_to_global(const char* lds, bf16* __restric
 // 8 (r/4) + 4 (l/32) + r % 4 of it.  So four consecutive registers are four
 // consecutive columns of one row: one 8-byte LDS write per four values, into
 // the same [col/64][row][64] slab layout as acc_to_slabs.
-template <int FM, int FN>
-__device__ __forceinline__ void acc_to_slabsT(const f32x16_t (&acc)[FM][FN], char* lds, int slab_bytes,
-                                              int rbase, int cbase, int lane) {
+template <int FM, int FN, bool SC>
+__device__ __forceinline__ void acc_to_slabsT_impl(const f32x16_t (&acc)[FM][FN], char* lds,
+                                                   int slab_bytes, int rbase, int cbase, int lane,
+                                                   const float* __restrict__ cs) {
   const int h = lane >> 5;
+  if constexpr (SC) {
+    // one scale vector (the lane's four columns c0 + 4 h .. + 3) at a time,
+    // used for every row fragment before the next is loaded
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c0 = cbase + j * 32 + 8 * q;
+        const float4 sc = *reinterpret_cast<const float4*>(cs + c0 + 4 * h);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const int row = rbase + i * 32 + (lane & 31);
+          const int key = (row ^ (row >> 3)) & 7;
+          uint2 v;
+          v.x = pack2bf(acc[i][j][4 * q] * sc.x, acc[i][j][4 * q + 1] * sc.y);
+          v.y = pack2bf(acc[i][j][4 * q + 2] * sc.z, acc[i][j][4 * q + 3] * sc.w);
+          *reinterpret_cast<uint2*>(lds + row * ROWB + 8 * h + (c0 >> 6) * slab_bytes +
+                                    ((((c0 & 63) >> 3) ^ key) << 4)) = v;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int row = rbase + i * 32 + (lane & 31);
@@ -187,6 +225,18 @@ __device__ __forceinline__ void acc_to_slabsT(const f32x16_t (&acc)[FM][FN], cha
         v.y = pack2bf(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
         *reinterpret_cast<uint2*>(rowp + (c0 >> 6) * slab_bytes + ((((c0 & 63) >> 3) ^ key) << 4)) = v;
       }
+  }
+}
+
+// cs (or null): column c of the tile scaled by cs[c] before rounding.
+template <int FM, int FN>
+__device__ __forceinline__ void acc_to_slabsT(const f32x16_t (&acc)[FM][FN], char* lds, int slab_bytes,
+                                              int rbase, int cbase, int lane,
+                                              const float* __restrict__ cs = nullptr) {
+  if (cs) {
+    acc_to_slabsT_impl<FM, FN, true>(acc, lds, slab_bytes, rbase, cbase, lane, cs);
+  } else {
+    acc_to_slabsT_impl<FM, FN, false>(acc, lds, slab_bytes, rbase, cbase, lane, cs);
   }
 }
 
@@ -231,12 +281,37 @@ __device__ __forceinline__ void slabs_to_global_buf(const char* lds, bf16* __res
   }
 }
 
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x8_t __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+// two transposed 4 x 16 reads -> one 8-value MFMA operand
+__device__ __forceinline__ bf16x8_t frag_tr(const char* p0, const char* p1) {
+  const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p0)));
+  const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p1)));
+  const s16x8_t w = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8_t, w);
+}
+
+// eight int8 values (K order, lowest byte first) as a bf16 MFMA operand;
+// exact, since every int8 value has at most 8 significant bits
+__device__ __forceinline__ bf16x8_t i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const int32_t a = (int32_t)lo, b = (int32_t)hi;
+  uint4 u;
+  u.x = pack2bf((float)((a << 24) >> 24), (float)((a << 16) >> 24));
+  u.y = pack2bf((float)((a << 8) >> 24), (float)(a >> 24));
+  u.z = pack2bf((float)((b << 24) >> 24), (float)((b << 16) >> 24));
+  u.w = pack2bf((float)((b << 8) >> 24), (float)(b >> 24));
+  return as_bf16x8(u);
+}
+
 // C = A B^T with register-staged loads (two LDS stages), for shapes k_nt4
 // does not take: fewer 256 x 256 tiles than CUs, or N % 256 != 0.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
     int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const bf16* __restrict__ B,
-    long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN) {
+    long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN,
+    const float* __restrict__ cscale, long sS) {
   using C = Cfg<BM, BN, WM, WN>;
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
@@ -295,7 +370,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
   // stage buffers) -> global with 16-byte stores over whole row segments
   constexpr int SLAB = BM * ROWB;
   static_assert(BN * SLAB / BK <= C::LDS, "staging fits in the stage buffers");
-  acc_to_slabs<C::FM, C::FN>(acc, smem, SLAB, wm * C::TM, wn * C::TN, lane, 0, BM);
+  acc_to_slabs<C::FM, C::FN>(acc, smem, SLAB, wm * C::TM, wn * C::TN, lane, 0, BM,
+                             cscale ? cscale + bt * sS + n0 : nullptr);
   __syncthreads();
   slabs_to_global<BM, BN, C::NTH>(smem, Cm, ldc, m0, n0, M, N);
 }
@@ -320,13 +396,37 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
 // store (buffer stores whose range covers the tile's existing rows).  The K
 // order of the MFMAs is plain ascending, as in k_gemm_nt.  EPI 1 adds the
 // block epilogue (described at its code below).
-template <int EPI>
+//
+// BMODE selects B's storage: 0 bf16 [N][K] (as above), 1 int8 [N][K], 2 bf16
+// [K][N] (K-major: the weight as stored for the other product, so one copy
+// serves both).
+// K-major B (BMODE 2): a 64-row K slab of the tile's 256 columns lands in the
+// B slot as 64 rows of 512 bytes, 16-byte chunk c of row k stored at
+// position c ^ 2 (k mod 4), and the fragments are read with
+// ds_read_b64_tr_b16: each 16-lane group receives a 4-K x 16-column tile
+// transposed, and two reads give a lane its eight consecutive K values of
+// one column, the same values in the same K order as the N-major read, so
+// the products are bitwise those of BMODE 0 on the transposed weight.
+// int8 B (BMODE 1; a quantized weight; ldb, sB in bytes).  Its
+// 64-wide K slabs land in the B slots as 64-byte rows (16 KB of the 32 KB
+// slot), 16-byte chunk c of row r stored at position c ^ ((r >> 2) & 3), and
+// are widened to bf16 when the fragments are read: every int8 value is
+// exact in bf16, so the products are those of the integer weight.  One
+// 16-byte read per row gives a lane the B values of two K-steps, so within
+// a slab a K-step pair 2j, 2j+1 takes, for lane half h, the K ranges
+// 32 j + 16 h + [0, 8) and + [8, 16); the A reads follow the same K order.
+// SC: column c of C is multiplied by cscale[bt * sS + c] (fp32, before
+// rounding), which applies a per-output-row weight scale.
+template <int EPI, int BMODE, bool SC>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nt4(
-    int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const bf16* __restrict__ B,
+    int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const void* __restrict__ Bv,
     long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN,
-    const bf16* __restrict__ Bk, bf16* __restrict__ E, long lde) {
+    const bf16* __restrict__ Bk, bf16* __restrict__ E, long lde, const float* __restrict__ cscale,
+    long sS) {
   constexpr int BM = 256, BN = 256, TM = 128, TN = 128, FM = 4, FN = 4, NTH = 256;
   constexpr int OPB = 256 * ROWB;  // one operand's 256 rows of a 64-wide slab: 32 KB
+  constexpr bool BQ = BMODE == 1, BNN = BMODE == 2;
+  constexpr int BES = BQ ? 1 : 2;  // bytes per B element
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
@@ -340,8 +440,12 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // bottom edge); offsets stay below 256 * ld * 2 < 2^31 (host-checked)
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(A + bt * sA + (long)m0 * lda), (short)0, min(BM, M - m0) * (int)lda * 2, 0x00020000);
+  // K-major B: the tile's columns from n0, every K row (K * ldb * 2 < 2^31,
+  // host-checked); N-major: the tile's rows that exist
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(B + bt * sB + (long)n0 * ldb), (short)0, min(BN, N - n0) * (int)ldb * 2, 0x00020000);
+      (void*)(reinterpret_cast<const char*>(Bv) +
+              (bt * sB + (BNN ? (long)n0 : (long)n0 * ldb)) * BES),
+      (short)0, BNN ? K * (int)ldb * 2 : min(BN, N - n0) * (int)ldb * BES, 0x00020000);
   // Load q (0..7) of this wave fills rows 32 q + 8 wave .. +7 of a slot
   // (1 KB): lane l lands at byte 16 l, i.e. row 32 q + 8 wave + l/8, slot
   // position l % 8, which holds logical chunk (l%8) ^ (l/8) ^ wave ^ 4 (q&1)
@@ -355,6 +459,27 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     voB[p] = rl * (int)ldb * 2 + ((cx ^ (4 * p)) << 4);
   }
   const int gA = 32 * (int)lda * 2, gB = 32 * (int)ldb * 2;  // bytes per 32 rows
+  // int8 B: load q (0..3) of this wave fills rows 64 q + 16 wave + l/4 of a
+  // slot (1 KB of 64-byte rows), lane l at position l % 4, which holds
+  // logical chunk (l % 4) ^ (l / 16) under the int8 swizzle
+  int voQ[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    voQ[q] = (64 * q + 16 * wave + lane / 4) * (int)ldb + 16 * ((lane & 3) ^ (lane >> 4));
+  // K-major B: load q (0..7) of this wave fills K rows 2 (4 q + wave) + l/32
+  // of the slab, lane l at chunk position l % 32, which holds logical chunk
+  // (l % 32) ^ 2 (row mod 4); a slab is 64 K rows further
+  int voN[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int row = 2 * (4 * q + wave) + lane / 32;
+    voN[q] = row * (int)ldb * 2 + 16 * ((lane & 31) ^ ((row & 3) << 1));
+  }
+  const int slabN = 64 * (int)ldb * 2;
+  // K-major fragment reads: lane l supplies K row 8 (l/32) + (l%16)/4 and
+  // columns 16 ((l>>4)&1) + 4 (l&3) .. +3 of a 32-column fragment
+  const int tk_l = 8 * (lane / 32) + (lane % 16) / 4;
+  const int ft_l = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   // load q of slab `from` into the slot at byte offset slotb.  M0 (the LDS
   // destination) is set inside the same asm statement; nothing else in these
   // kernels reads M0 (no indirect register indexing, no LDS-DMA builtins),
@@ -367,17 +492,52 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
                  "v"(vo[(q) & 1] + (q) * (g) + (from) * 128), "s"(rs)                          \
                  : "memory");                                                                 \
   }
+  // int8 B, slab `from`, load q into the slot at byte offset slotb
+#define POETX_DMAQ(slotb, from, q)                                                             \
+  {                                                                                            \
+    const uint32_t m0v_ =                                                                      \
+        __builtin_amdgcn_readfirstlane(lds0 + (slotb) + ((q) * 4 + wave) * 1024);              \
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v_),    \
+                 "v"(voQ[q] + (from) * 64), "s"(rsB)                                           \
+                 : "memory");                                                                 \
+  }
+  // K-major bf16 B, slab `from`, load q into the slot at byte offset slotb
+#define POETX_DMAN(slotb, from, q)                                                             \
+  {                                                                                            \
+    const uint32_t m0v_ =                                                                      \
+        __builtin_amdgcn_readfirstlane(lds0 + (slotb) + ((q) * 4 + wave) * 1024);              \
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds" ::"s"(m0v_),    \
+                 "v"(voN[q] + (from) * slabN), "s"(rsB)                                        \
+                 : "memory");                                                                 \
+  }
   // operand fragment g of K-step ks from slots sa (A) / sb (B): g < 4 reads A
-  // rows, else B rows
+  // rows, else B rows.  int8 B: the even K-step of a pair reads both steps'
+  // bytes, widens its own half and keeps the other for the odd step.
+  // K-major B: two transposed reads, K rows t0 and t0 + 4.
 #define POETX_FRAG(F, sa, sb, ks, g)                                                           \
   {                                                                                            \
-    const int c_ = (ks) * 2 + lane / 32;                                                       \
-    if ((g) < 4)                                                                               \
+    if ((g) < 4) {                                                                             \
+      const int c_ = BQ ? 4 * ((ks) >> 1) + 2 * (lane / 32) + ((ks) & 1) : (ks) * 2 + lane / 32; \
       fa[F][(g) & 3] = as_bf16x8(*reinterpret_cast<const uint4*>(                              \
           smem + (sa) + lds_off(wm * TM + ((g) & 3) * 32 + lane % 32, c_)));                    \
-    else                                                                                       \
+    } else if (BNN) {                                                                          \
+      const int ft_ = wn * TN + ((g) & 3) * 32 + ft_l;                                         \
+      const int t0_ = 16 * (ks) + tk_l, t1_ = t0_ + 4;                                         \
+      fb[F][(g) & 3] = frag_tr(                                                                \
+          smem + (sb) + t0_ * 512 + ((((ft_ >> 3) ^ ((t0_ & 3) << 1))) << 4) + (ft_ & 7) * 2,  \
+          smem + (sb) + t1_ * 512 + ((((ft_ >> 3) ^ ((t1_ & 3) << 1))) << 4) + (ft_ & 7) * 2); \
+    } else if (!BQ) {                                                                          \
       fb[F][(g) & 3] = as_bf16x8(*reinterpret_cast<const uint4*>(                              \
-          smem + (sb) + lds_off(wn * TN + ((g) & 3) * 32 + lane % 32, c_)));                    \
+          smem + (sb) + lds_off(wn * TN + ((g) & 3) * 32 + lane % 32, (ks) * 2 + lane / 32)));  \
+    } else if (((ks) & 1) == 0) {                                                              \
+      const int r_ = wn * TN + ((g) & 3) * 32 + lane % 32;                                     \
+      const uint4 raw_ = *reinterpret_cast<const uint4*>(                                      \
+          smem + (sb) + r_ * 64 + 16 * (((ks) + lane / 32) ^ ((r_ >> 2) & 3)));                \
+      fb[F][(g) & 3] = i8x8_to_bf16(raw_.x, raw_.y);                                           \
+      fbq[(g) & 3] = make_uint2(raw_.z, raw_.w);                                               \
+    } else {                                                                                   \
+      fb[F][(g) & 3] = i8x8_to_bf16(fbq[(g) & 3].x, fbq[(g) & 3].y);                           \
+    }                                                                                          \
   }
   // MFMAs 2g, 2g+1 of a K-step: row fragment g/2 against two column
   // fragments, which run 0..3 for even rows and 3..0 for odd ones, so that
@@ -399,6 +559,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = (f32x16_t){};
   bf16x8_t fa[2][FM], fb[2][FN];
+  uint2 fbq[FN];  // int8 B: the odd K-step's raw bytes
   const int nk = K / 64;
   // Slab numbers past the end are clamped to the last slab; those copies land
   // in slots that are never read again, so every wave always has the same
@@ -407,14 +568,32 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     const int s1 = min(1, nk - 1);
 #pragma unroll
     for (int q = 0; q < 8; ++q) POETX_DMA1(0 * OPB, 0, q, voA, gA, rsA);
+    if constexpr (BQ) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) POETX_DMA1(1 * OPB, 0, q, voB, gB, rsB);
+      for (int q = 0; q < 4; ++q) POETX_DMAQ(1 * OPB, 0, q);
+    } else if constexpr (BNN) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) POETX_DMAN(1 * OPB, 0, q);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) POETX_DMA1(1 * OPB, 0, q, voB, gB, rsB);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) POETX_DMA1(2 * OPB, s1, q, voA, gA, rsA);
+    if constexpr (BQ) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) POETX_DMA1(3 * OPB, s1, q, voB, gB, rsB);
+      for (int q = 0; q < 4; ++q) POETX_DMAQ(3 * OPB, s1, q);
+    } else if constexpr (BNN) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) POETX_DMAN(3 * OPB, s1, q);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) POETX_DMA1(3 * OPB, s1, q, voB, gB, rsB);
+    }
   }
-  asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // slab 0 has landed (this wave's part)
+  // slab 0 has landed (this wave's part): at most slab 1's loads are pending
+  if constexpr (BQ) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < 8; ++g) POETX_FRAG(0, 0, OPB, 0, g);
@@ -456,19 +635,31 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     for (int g = 0; g < 8; ++g) {
       POETX_FRAG(0, na, nb, 0, g);
       POETX_MMA2(1, g);
-      POETX_DMA1(sa, pre, g, voB, gB, rsB);
+      if constexpr (BQ) {
+        if ((g & 1) == 0) POETX_DMAQ(sa, pre, g / 2);
+      } else if constexpr (BNN) {
+        POETX_DMAN(sa, pre, g);
+      } else {
+        POETX_DMA1(sa, pre, g, voB, gB, rsB);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     sl = sl + 2 >= 5 ? sl - 3 : sl + 2;
   }
 #undef POETX_DMA1
+#undef POETX_DMAQ
+#undef POETX_DMAN
 #undef POETX_FRAG
 #undef POETX_MMA2
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   constexpr int SLAB = BM * ROWB;
-  acc_to_slabsT<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane);
+  if constexpr (SC)
+    acc_to_slabsT_impl<FM, FN, true>(acc, smem, SLAB, wm * TM, wn * TN, lane,
+                                     cscale + bt * sS + n0);
+  else
+    acc_to_slabsT<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane);
   // Block epilogue, E = C_tile blockdiag(G)^T, formed transposed like C.
   // EPI 1 (blocks of 256): the tile's columns are one block, so every wave
   // sums over all 256 columns of the C tile with G block tn.  EPI 2 (blocks
@@ -534,17 +725,6 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   }
 }
 
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef short s16x8_t __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
-
-// two transposed 4 x 16 reads -> one 8-value MFMA operand
-__device__ __forceinline__ bf16x8_t frag_tr(const char* p0, const char* p1) {
-  const s16x4_t h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p0)));
-  const s16x4_t h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(const_cast<char*>(p1)));
-  const s16x8_t w = __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8_t, w);
-}
 
 // Token reduction P[s][bt][r][c] = sum over split s's tokens of
 // A[t][bt*sA + tr*TILE + r] * B[t][bt*sB + tc*TILE + c]  (dG = dS^T Z, dV^T U).
@@ -808,7 +988,8 @@ template <int B, int TOK, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, int tiles_per_wg,
                                                             const bf16* __restrict__ A,
                                                             const bf16* __restrict__ G,
-                                                            bf16* __restrict__ Out) {
+                                                            bf16* __restrict__ Out,
+                                                            const float* __restrict__ cscale) {
   constexpr int NTH = 64 * WM * WN;
   constexpr int TM = TOK / WM, TN = B / WN, FM = TM / 32, FN = TN / 32;
   constexpr int NS = B / BK;                    // K-slabs per token tile
@@ -894,7 +1075,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
 #pragma unroll
           for (int p = 0; p < TOK / PROWS; ++p) {
             acc_to_slabs<FM, FN>(acc, stg, PROWS * ROWB, wm * TM, wn * TN, lane, p * PROWS,
-                                 (p + 1) * PROWS);
+                                 (p + 1) * PROWS, cscale ? cscale + (long)j * B : nullptr);
             __syncthreads();
             slabs_to_global_buf<PROWS, B, NTH>(stg, Oj, width, t0 + p * PROWS, 0, T);
             __syncthreads();
@@ -939,16 +1120,18 @@ hipError_t set_lds(K kern, int bytes) {
 
 template <int BM, int BN, int WM, int WN>
 hipError_t nt_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA, const bf16* B,
-                     long ldb, long sB, bf16* C, long ldc, long sC, hipStream_t s) {
+                     long ldb, long sB, bf16* C, long ldc, long sC, hipStream_t s,
+                     const float* cscale, long sS) {
   using CF = Cfg<BM, BN, WM, WN>;
   auto kern = k_gemm_nt<BM, BN, WM, WN>;
+  if (cscale && N % BN) return hipErrorInvalidValue;  // the scale is read for whole tiles
   constexpr int lds = CF::LDS;
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
   hipLaunchKernelGGL(kern, dim3(tilesM * tilesN, batch), dim3(CF::NTH), lds, s, M, N, K, A, lda,
-                     sA, B, ldb, sB, C, ldc, sC, tilesM, tilesN);
+                     sA, B, ldb, sB, C, ldc, sC, tilesM, tilesN, cscale, sS);
   return hipGetLastError();
 }
 
@@ -985,36 +1168,53 @@ bool nt4_ld_ok(long lda, long ldb, long ldc) {
 }
 
 // 4-wave 256 x 256 launcher; LDS: the five 32 KB operand slots (the block
-// epilogue stages its tile in the first 128 KB)
-template <int EPI>
-hipError_t nt4_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
-                      const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC, const bf16* Bk,
-                      bf16* E, long lde, hipStream_t s) {
-  auto kern = k_nt4<EPI>;
+// epilogue stages its tile in the first 128 KB).  BMODE: B's storage (k_nt4).
+template <int EPI, int BMODE = 0, bool SC = false>
+hipError_t nt4_launch_t(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
+                        const void* B, long ldb, long sB, bf16* C, long ldc, long sC,
+                        const bf16* Bk, bf16* E, long lde, hipStream_t s, const float* cscale,
+                        long sS) {
+  auto kern = k_nt4<EPI, BMODE, SC>;
   constexpr int lds = 5 * 256 * ROWB;
   static_assert(lds <= 160 * 1024, "LDS budget");
   static const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
   const int tM = (M + 255) / 256, tN = (N + 255) / 256;
   hipLaunchKernelGGL(kern, dim3(tM * tN, batch), dim3(256), lds, s, M, N, K, A, lda, sA, B, ldb,
-                     sB, C, ldc, sC, tM, tN, Bk, E, lde);
+                     sB, C, ldc, sC, tM, tN, Bk, E, lde, cscale, sS);
   return hipGetLastError();
+}
+
+// the column scale is a compile-time choice: the scaled staging costs
+// registers the plain kernels do not spend
+template <int EPI, int BMODE = 0>
+hipError_t nt4_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
+                      const void* B, long ldb, long sB, bf16* C, long ldc, long sC, const bf16* Bk,
+                      bf16* E, long lde, hipStream_t s, const float* cscale = nullptr,
+                      long sS = 0) {
+  if (cscale)
+    return nt4_launch_t<EPI, BMODE, true>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, Bk, E,
+                                       lde, s, cscale, sS);
+  return nt4_launch_t<EPI, BMODE, false>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, Bk, E,
+                                      lde, s, nullptr, 0);
 }
 
 hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
-                          hipStream_t s) {
+                          hipStream_t s, const float* cscale, long sS) {
   auto tiles = [&](int bm, int bn) { return (long)batch * ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
   // the 256 x 256 kernel stays ahead of the 256 x 128 one down to half a
   // tile per CU (4096 x 2048 x 2048: 43 against 52 us)
   if (N % 256 == 0 && tiles(256, 256) >= NUM_CU / 2 && nt4_ld_ok(lda, ldb, ldc))
     return nt4_launch<0>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, nullptr, nullptr, 0,
-                         s);
+                         s, cscale, sS);
   if (N % 128 == 0 && tiles(256, 128) >= NUM_CU)
-    return nt_launch<256, 128, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+    return nt_launch<256, 128, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s, cscale,
+                                     sS);
   if (N % 128 == 0)
-    return nt_launch<128, 128, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
-  return nt_launch<128, 64, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s);
+    return nt_launch<128, 128, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s, cscale,
+                                     sS);
+  return nt_launch<128, 64, 2, 2>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, s, cscale, sS);
 }
 
 bool mfma_nt_block_ok(int M, int N, int K, int b) {
@@ -1031,11 +1231,47 @@ hipError_t launch_mfma_nt_block(int M, int N, int K, int b, const bf16* A, long 
   return nt4_launch<1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
 }
 
+bool mfma_nt_kmajor_ok(int M, int N, int K, long lda, long ldb, long ldc) {
+  return M > 0 && N % 256 == 0 && K % BK == 0 && nt4_ld_ok(lda, ldb, ldc) && ldb >= N &&
+         (long)K * ldb * 2 < (1L << 31);
+}
+
+hipError_t launch_mfma_nt_kmajor(int M, int N, int K, int b, const bf16* A, long lda,
+                                 const bf16* Bkn, long ldb, bf16* C, long ldc, const bf16* Bk,
+                                 bf16* E, long lde, hipStream_t s) {
+  if (!mfma_nt_kmajor_ok(M, N, K, lda, ldb, ldc) || (E && !nt4_ld_ok(lda, ldb, lde)))
+    return hipErrorInvalidValue;
+  if (!E)
+    return nt4_launch<0, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s);
+  if (b == 128)
+    return nt4_launch<2, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+  if (b != 256) return hipErrorInvalidValue;
+  return nt4_launch<1, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+}
+
+bool mfma_nt_q_ok(int M, int N, int K, long lda, long ldb, long ldc) {
+  return M > 0 && N % 256 == 0 && K % BK == 0 && nt4_ld_ok(lda, ldb, ldc);
+}
+
+hipError_t launch_mfma_nt_q(int M, int N, int K, int b, const bf16* A, long lda, const int8_t* Bq,
+                            long ldb, bf16* C, long ldc, const float* cscale, const bf16* Bk,
+                            bf16* E, long lde, hipStream_t s) {
+  if (!mfma_nt_q_ok(M, N, K, lda, ldb, ldc) || (E && !nt4_ld_ok(lda, ldb, lde)))
+    return hipErrorInvalidValue;
+  if (!E)
+    return nt4_launch<0, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s,
+                               cscale, 0);
+  if (b == 128)
+    return nt4_launch<2, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, Bk, E, lde, s, cscale, 0);
+  if (b != 256) return hipErrorInvalidValue;
+  return nt4_launch<1, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, Bk, E, lde, s, cscale, 0);
+}
+
 bool mfma_blocks_ok(int b) { return b == 128 || b == 256; }
 
 template <int B, int TOK, int WM, int WN>
 hipError_t blocks_launch(int nblk, int T, int width, const bf16* A, const bf16* G, bf16* Out,
-                         hipStream_t s) {
+                         hipStream_t s, const float* cscale) {
   auto kern = k_blocks<B, TOK, WM, WN>;
   constexpr int lds = B * B * 2 + 2 * TOK * ROWB;
   static_assert(lds <= 160 * 1024, "LDS budget");
@@ -1055,15 +1291,15 @@ hipError_t blocks_launch(int nblk, int T, int width, const bf16* A, const bf16* 
     if (best < 0 || cost < best || (cost == best && sp < splits)) best = cost, per = p, splits = sp;
   }
   hipLaunchKernelGGL(kern, dim3(nblk, splits), dim3(64 * WM * WN), lds, s, T, width, per, A, G,
-                     Out);
+                     Out, cscale);
   return hipGetLastError();
 }
 
 hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, const bf16* G,
-                              bf16* Out, hipStream_t s) {
+                              bf16* Out, hipStream_t s, const float* cscale) {
   if (width <= 0 || width >= (1 << 21)) return hipErrorInvalidValue;  // 32-bit buffer offsets
-  if (b == 256) return blocks_launch<256, 128, 2, 4>(nblk, T, width, A, G, Out, s);
-  if (b == 128) return blocks_launch<128, 256, 4, 2>(nblk, T, width, A, G, Out, s);
+  if (b == 256) return blocks_launch<256, 128, 2, 4>(nblk, T, width, A, G, Out, s, cscale);
+  if (b == 128) return blocks_launch<128, 256, 4, 2>(nblk, T, width, A, G, Out, s, cscale);
   return hipErrorInvalidValue;
 }
 

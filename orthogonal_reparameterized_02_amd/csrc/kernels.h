@@ -41,11 +41,12 @@ hipError_t launch_gather_f32(int n, const float* src, const int32_t* idx, float*
                              hipStream_t s);
 
 // ---- portable tiled kernels (simple.hip) ----------------------------------
-// C[bt][i][j] = sum_k A[bt][i][k] * B[bt][j][k]       (row-major, fp32 accumulate)
+// C[bt][i][j] = sum_k A[bt][i][k] * B[bt][j][k]       (row-major, fp32 accumulate);
+// bkmajor: B given K-major, element (j, k) at B[bt][k * ldb + j]
 template <typename TS>
 hipError_t launch_simple_nt(int batch, int M, int N, int K, const TS* A, long lda,
                             long sA, const TS* B, long ldb, long sB, TS* C, long ldc,
-                            long sC, hipStream_t s);
+                            long sC, hipStream_t s, bool bkmajor = false);
 // C[bt][i][j] = sum_k A[bt][k][i] * B[bt][k][j]       (float32 output)
 template <typename TS>
 hipError_t launch_simple_tn(int batch, int M, int N, int K, const TS* A, long lda,
@@ -62,10 +63,11 @@ hipError_t launch_cnp_small_bwd(int nblk, int b, int k, const float* theta, cons
 // ---- bf16 MFMA GEMMs (gemm_mfma.hip) --------------------------------------
 // usable when N % 64 == 0 and K % 64 == 0 (M any)
 bool mfma_nt_ok(int M, int N, int K);
-// C[bt] = A[bt] B[bt]^T; A [M][K] (row pitch lda), B [N][K] (ldb), C [M][N] (ldc)
+// C[bt] = A[bt] B[bt]^T; A [M][K] (row pitch lda), B [N][K] (ldb), C [M][N] (ldc);
+// cscale (or null): column c of C[bt] scaled by cscale[bt * sS + c] before rounding
 hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                           const bf16* B, long ldb, long sB, bf16* C, long ldc, long sC,
-                          hipStream_t s);
+                          hipStream_t s, const float* cscale = nullptr, long sS = 0);
 // C = A B^T as above (one batch) and, per b-column block g of C (b = 256 or
 // 128), E[:, g] = C[:, g] Bk[g]^T with Bk [N/b][b][b].
 // E == nullptr: C only, from the same main loop (bitwise the same C).
@@ -73,11 +75,28 @@ bool mfma_nt_block_ok(int M, int N, int K, int b);
 hipError_t launch_mfma_nt_block(int M, int N, int K, int b, const bf16* A, long lda,
                                 const bf16* B, long ldb, bf16* C, long ldc, const bf16* Bk,
                                 bf16* E, long lde, hipStream_t s);
+// C = A B^T with B given K-major, Bkn = B^T [K][N] (row pitch ldb >= N):
+// the dense product of the backward, dV = dZ W0f, read from W0f itself;
+// bitwise the result of launch_mfma_nt_block on the transposed copy, block
+// epilogue included.  N % 256 == 0, K % 64 == 0, K ldb 2 < 2^31.
+bool mfma_nt_kmajor_ok(int M, int N, int K, long lda, long ldb, long ldc);
+hipError_t launch_mfma_nt_kmajor(int M, int N, int K, int b, const bf16* A, long lda,
+                                 const bf16* Bkn, long ldb, bf16* C, long ldc, const bf16* Bk,
+                                 bf16* E, long lde, hipStream_t s);
+// C = (A Bq^T) diag(cscale) for an int8 Bq [N][K] (row pitch ldb bytes): the
+// dense product on a quantized weight, widened to bf16 inside the kernel's
+// operand path (exact) with the per-row weight scale applied to the fp32
+// sums; with E, the block epilogue of launch_mfma_nt_block on the scaled C.
+bool mfma_nt_q_ok(int M, int N, int K, long lda, long ldb, long ldc);
+hipError_t launch_mfma_nt_q(int M, int N, int K, int b, const bf16* A, long lda, const int8_t* Bq,
+                            long ldb, bf16* C, long ldc, const float* cscale, const bf16* Bk,
+                            bf16* E, long lde, hipStream_t s);
 // per-token block products for b in {128, 256}:
-// Out[t][j b + n] = sum_k A[t][j b + k] G[j][n][k]  (A, Out row pitch `width`)
+// Out[t][j b + n] = sum_k A[t][j b + k] G[j][n][k]  (A, Out row pitch `width`),
+// column c of Out scaled by cscale[c] before rounding when cscale is set
 bool mfma_blocks_ok(int b);
 hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, const bf16* G,
-                              bf16* Out, hipStream_t s);
+                              bf16* Out, hipStream_t s, const float* cscale = nullptr);
 // out[bt][r][c] = sum_t A[t][bt*sA + r] B[t][bt*sB + c], D x D per batch,
 // D in {64, 128, 256, 512}; partials: tn_partial_bytes(batch, D, T,
 // max(lda, ldb)) bytes.  D >= 256: sA = sB = D; the token splits are sized

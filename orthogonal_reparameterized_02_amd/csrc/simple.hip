@@ -10,12 +10,13 @@ namespace {
 
 constexpr int TILE = 16;
 
-// C[bt][i][j] = sum_k A[bt][i][k] * B[bt][j][k]
+// C[bt][i][j] = sum_k A[bt][i][k] * B[bt][j][k]; bkm: B given K-major,
+// element (j, k) at B[bt][k * ldb + j]
 template <typename TS>
 __global__ __launch_bounds__(256) void k_simple_nt(int M, int N, int K, const TS* __restrict__ A,
                                                    long lda, long sA, const TS* __restrict__ B,
                                                    long ldb, long sB, TS* __restrict__ C, long ldc,
-                                                   long sC) {
+                                                   long sC, int bkm) {
   __shared__ float As[TILE][TILE + 1];
   __shared__ float Bs[TILE][TILE + 1];
   const int bt = blockIdx.z;
@@ -29,8 +30,13 @@ __global__ __launch_bounds__(256) void k_simple_nt(int M, int N, int K, const TS
   for (int k0 = 0; k0 < K; k0 += TILE) {
     int ar = blockIdx.y * TILE + ty, ac = k0 + tx;
     As[ty][tx] = (ar < M && ac < K) ? St<TS>::ld(A + ar * lda + ac) : 0.f;
-    int br = blockIdx.x * TILE + ty, bc = k0 + tx;
-    Bs[ty][tx] = (br < N && bc < K) ? St<TS>::ld(B + br * ldb + bc) : 0.f;
+    if (bkm) {  // row k0 + ty of the K-major B, coalesced along j
+      const int kr = k0 + ty, jc = blockIdx.x * TILE + tx;
+      Bs[tx][ty] = (jc < N && kr < K) ? St<TS>::ld(B + kr * ldb + jc) : 0.f;
+    } else {
+      const int br = blockIdx.x * TILE + ty, bc = k0 + tx;
+      Bs[ty][tx] = (br < N && bc < K) ? St<TS>::ld(B + br * ldb + bc) : 0.f;
+    }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < TILE; ++kk) acc += As[ty][kk] * Bs[tx][kk];
@@ -182,10 +188,10 @@ __global__ __launch_bounds__(256) void k_cnp_small_bwd(int b, int k, const float
 template <typename TS>
 hipError_t launch_simple_nt(int batch, int M, int N, int K, const TS* A, long lda, long sA,
                             const TS* B, long ldb, long sB, TS* C, long ldc, long sC,
-                            hipStream_t s) {
+                            hipStream_t s, bool bkmajor) {
   dim3 grid((N + TILE - 1) / TILE, (M + TILE - 1) / TILE, batch);
   hipLaunchKernelGGL(k_simple_nt<TS>, grid, dim3(256), 0, s, M, N, K, A, lda, sA, B, ldb, sB, C,
-                     ldc, sC);
+                     ldc, sC, bkmajor ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -217,10 +223,10 @@ hipError_t launch_cnp_small_bwd(int nblk, int b, int k, const float* theta, cons
 
 template hipError_t launch_simple_nt<float>(int, int, int, int, const float*, long, long,
                                             const float*, long, long, float*, long, long,
-                                            hipStream_t);
+                                            hipStream_t, bool);
 template hipError_t launch_simple_nt<bf16>(int, int, int, int, const bf16*, long, long,
                                            const bf16*, long, long, bf16*, long, long,
-                                           hipStream_t);
+                                           hipStream_t, bool);
 template hipError_t launch_simple_tn<float>(int, int, int, int, const float*, long, long,
                                             const float*, long, long, float*, long, long,
                                             hipStream_t);

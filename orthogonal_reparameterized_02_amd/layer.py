@@ -24,12 +24,15 @@ class POETXLayer:
     """Buffers and calls for one (m, n, b, k, T, dtype) layer."""
 
     def __init__(self, m: int, n: int, b: int, k: int, T: int, act: int, device="cuda",
-                 xmem: bool = False, xq: bool = False):
+                 xmem: bool = False, xq: bool = False, keep_w0ft: bool = False):
         """xmem: keep only U for the backward pass and recompute Z there
         (the memory-saving mode) instead of keeping U and Z.
-        xq: the base weight is int8 with per-row scales (load_q); each pass
-        expands the folded int8 weight to bf16 in W0f / W0fT just before
-        the layer call (a multi-layer runtime would share those buffers)."""
+        xq: the base weight is int8 with per-row scales (load_q); the dense
+        products read the folded int8 weight directly and no bf16 copy of
+        it is kept (W0f and W0fT are None).
+        keep_w0ft: also keep the folded weight transposed (W0fT) for the
+        backward's dense product; by default it reads W0f itself, so the
+        fixed weight is held once (same results, bit for bit)."""
         self.m, self.n, self.b, self.k, self.T, self.act = m, n, b, k, T, act
         self.xmem, self.xq = xmem, xq
         if xq and act != P.BF16:
@@ -40,7 +43,8 @@ class POETXLayer:
         nP, nR = n // b, m // b
         self.nP, self.nR = nP, nR
         e = lambda *s, d=dt: torch.empty(*s, dtype=d, device=dev)
-        self.W0f, self.W0fT = e(m, n), e(n, m)
+        self.W0f = None if xq else e(m, n)
+        self.W0fT = e(n, m) if keep_w0ft and not xq else None
         if xq:
             self.qf, self.qfT = e(m, n, d=torch.int8), e(n, m, d=torch.int8)
             self.s_f = e(m, d=torch.float32)
@@ -90,6 +94,9 @@ class POETXLayer:
     def merge(self, out: torch.Tensor = None) -> torch.Tensor:
         """The weight R W0 P that the current theta and permutations
         represent (G from the latest cnp()), as an [m, n] tensor."""
+        if self.xq:
+            raise NotImplementedError("merging into an int8 base weight needs a new "
+                                      "quantization; not provided")
         if out is None:
             out = torch.empty(self.m, self.n, dtype=self.dtype, device=self.device)
         ws = _bytes(P.poetx_workspace_bytes(self.sh, 4), self.device)
@@ -133,7 +140,9 @@ class POETXLayer:
     def layer_fwd(self, x: torch.Tensor) -> None:
         """The layer forward alone (G_P, G_R already formed)."""
         if self.xq:
-            P.poetx_dequant(self.qf, self.s_f, True, self.W0f)
+            P.poetx_layer_fwd_q(self.sh, x, self.G_P, self.G_R, self.qf, self.s_f, self.perm_P,
+                                self.perm_R_inv, self.y, self.saved, self.ws_fwd, self.xmem)
+            return
         fwd = P.poetx_layer_fwd_xmem if self.xmem else P.poetx_layer_fwd
         fwd(self.sh, x, self.G_P, self.G_R, self.W0f, self.perm_P, self.perm_R_inv, self.y,
             self.saved, self.ws_fwd)
@@ -141,15 +150,17 @@ class POETXLayer:
     def layer_bwd(self, dy: torch.Tensor) -> None:
         """The layer backward alone (dx, dG_P, dG_R)."""
         if self.xq:
-            P.poetx_dequant(self.qfT, self.s_f, False, self.W0fT)
-        if self.xmem:
+            P.poetx_layer_bwd_q(self.sh, dy, self.G_P, self.GT_P, self.GT_R, self.qf, self.qfT,
+                                self.s_f, self.perm_P_inv, self.perm_R, self.saved, self.dx,
+                                self.dG_P, self.dG_R, self.ws_bwd, self.xmem)
+        elif self.xmem:
             P.poetx_layer_bwd_xmem(self.sh, dy, self.G_P, self.GT_P, self.GT_R, self.W0f,
                                    self.W0fT, self.perm_P_inv, self.perm_R, self.saved, self.dx,
                                    self.dG_P, self.dG_R, self.ws_bwd)
         else:
-            P.poetx_layer_bwd(self.sh, dy, self.GT_P, self.GT_R, self.W0fT, self.perm_P_inv,
-                              self.perm_R, self.saved, self.dx, self.dG_P, self.dG_R,
-                              self.ws_bwd)
+            P.poetx_layer_bwd(self.sh, dy, self.GT_P, self.GT_R, self.W0f, self.W0fT,
+                              self.perm_P_inv, self.perm_R, self.saved, self.dx, self.dG_P,
+                              self.dG_R, self.ws_bwd)
 
     def backward(self, dy: torch.Tensor):
         self.layer_bwd(dy)
@@ -212,8 +223,8 @@ class _POETXFn(torch.autograd.Function):
         dx = torch.empty(T, n, dtype=mod.dtype, device=dev)
         dG = torch.empty(theta.shape[0], b, b, dtype=torch.float32, device=dev)
         ws = _bytes(P.poetx_workspace_bytes(sh, 1), dev)
-        P.poetx_layer_bwd(sh, dy2, GT[:nP], GT[nP:], mod.W0fT, mod.perm_P_inv, mod.perm_R, saved,
-                          dx, dG[:nP], dG[nP:], ws)
+        P.poetx_layer_bwd(sh, dy2, GT[:nP], GT[nP:], mod.W0f, None, mod.perm_P_inv, mod.perm_R,
+                          saved, dx, dG[:nP], dG[nP:], ws)
         del ws
         dtheta = torch.empty_like(theta)
         # ws_cnp still holds this call's own unpacked Q
@@ -246,7 +257,7 @@ class POETXLinear(torch.nn.Module):
         self.theta_P = torch.nn.Parameter(torch.zeros(n // b, tb, device=device))
         self.theta_R = torch.nn.Parameter(torch.zeros(m // b, tb, device=device))
         e = lambda *s, d=dtype: torch.empty(*s, dtype=d, device=device)
-        self.W0f, self.W0fT = e(m, n), e(n, m)
+        self.W0f = e(m, n)
         self.perm_P, self.perm_R = e(n, d=torch.int32), e(m, d=torch.int32)
         self.perm_P_inv, self.perm_R_inv = e(n, d=torch.int32), e(m, d=torch.int32)
         self._gen = g
@@ -256,7 +267,7 @@ class POETXLinear(torch.nn.Module):
         """Draw new permutations and fold them into the weight."""
         self.perm_P.copy_(torch.randperm(self.n, generator=self._gen).to(torch.int32))
         self.perm_R.copy_(torch.randperm(self.m, generator=self._gen).to(torch.int32))
-        P.poetx_fold_perm(self.W0, self.perm_R, self.perm_P, self.W0f, self.W0fT,
+        P.poetx_fold_perm(self.W0, self.perm_R, self.perm_P, self.W0f, None,
                           self.perm_R_inv, self.perm_P_inv)
 
     @torch.no_grad()

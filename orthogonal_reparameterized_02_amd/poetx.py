@@ -146,8 +146,9 @@ def poetx_layer_fwd(sh: Shape, x, G_P, G_R, W0f, perm_P, perm_R_inv, y, saved, w
         _dev(y, "y", dt, T * m), _dev(saved, "saved"), wp, wb, _stream(stream)))
 
 
-def poetx_layer_bwd(sh: Shape, dy, GT_P, GT_R, W0fT, perm_P_inv, perm_R, saved, dx, dG_P, dG_R,
-                    ws, stream=None) -> None:
+def poetx_layer_bwd(sh: Shape, dy, GT_P, GT_R, W0f, W0fT, perm_P_inv, perm_R, saved, dx, dG_P,
+                    dG_R, ws, stream=None) -> None:
+    """W0fT may be None: the dense product then reads W0f K-major."""
     dt = _DT[sh.act]
     m, n, b, T = sh.m, sh.n, sh.b, sh.T
     need_ws, need_saved = poetx_workspace_bytes(sh, 1), poetx_saved_bytes(sh)
@@ -156,7 +157,8 @@ def poetx_layer_bwd(sh: Shape, dy, GT_P, GT_R, W0fT, perm_P_inv, perm_R, saved, 
         raise ValueError(f"saved: {need_saved} bytes required")
     check("poetx_layer_bwd", lib().poetx_layer_bwd(
         C.byref(sh), _dev(dy, "dy", dt, T * m), _dev(GT_P, "GT_P", dt, n * b),
-        _dev(GT_R, "GT_R", dt, m * b), _dev(W0fT, "W0fT", dt, m * n),
+        _dev(GT_R, "GT_R", dt, m * b), _dev(W0f, "W0f", dt, m * n),
+        _dev(W0fT, "W0fT", dt, m * n, optional=True),
         _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(perm_R, "perm_R", torch.int32, m),
         _dev(saved, "saved"), _dev(dx, "dx", dt, T * n), _dev(dG_P, "dG_P", torch.float32, n * b),
         _dev(dG_R, "dG_R", torch.float32, m * b), wp, wb, _stream(stream)))
@@ -188,10 +190,49 @@ def poetx_layer_bwd_xmem(sh: Shape, dy, G_P, GT_P, GT_R, W0f, W0fT, perm_P_inv, 
     check("poetx_layer_bwd_xmem", lib().poetx_layer_bwd_xmem(
         C.byref(sh), _dev(dy, "dy", dt, T * m), _dev(G_P, "G_P", dt, n * b),
         _dev(GT_P, "GT_P", dt, n * b), _dev(GT_R, "GT_R", dt, m * b),
-        _dev(W0f, "W0f", dt, m * n), _dev(W0fT, "W0fT", dt, m * n),
+        _dev(W0f, "W0f", dt, m * n), _dev(W0fT, "W0fT", dt, m * n, optional=True),
         _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(perm_R, "perm_R", torch.int32, m),
         _dev(saved, "saved"), _dev(dx, "dx", dt, T * n), _dev(dG_P, "dG_P", torch.float32, n * b),
         _dev(dG_R, "dG_R", torch.float32, m * b), wp, wb, _stream(stream)))
+
+
+def poetx_layer_fwd_q(sh: Shape, x, G_P, G_R, q_f, s_f, perm_P, perm_R_inv, y, saved, ws,
+                      xmem: bool = False, stream=None) -> None:
+    """The forward pass on an int8 base weight W0f = diag(s_f) q_f."""
+    dt = _DT[sh.act]
+    m, n, b, T = sh.m, sh.n, sh.b, sh.T
+    need_ws = poetx_workspace_bytes(sh, 2 if xmem else 0)
+    need_saved = poetx_saved_bytes_xmem(sh) if xmem else poetx_saved_bytes(sh)
+    wp, wb = _ws(ws, need_ws)
+    if saved.numel() * saved.element_size() < need_saved:
+        raise ValueError(f"saved: {need_saved} bytes required")
+    check("poetx_layer_fwd_q", lib().poetx_layer_fwd_q(
+        C.byref(sh), _dev(x, "x", dt, T * n), _dev(G_P, "G_P", dt, n * b),
+        _dev(G_R, "G_R", dt, m * b), _dev(q_f, "q_f", torch.int8, m * n),
+        _dev(s_f, "s_f", torch.float32, m), _dev(perm_P, "perm_P", torch.int32, n),
+        _dev(perm_R_inv, "perm_R_inv", torch.int32, m), _dev(y, "y", dt, T * m),
+        _dev(saved, "saved"), wp, wb, int(bool(xmem)), _stream(stream)))
+
+
+def poetx_layer_bwd_q(sh: Shape, dy, G_P, GT_P, GT_R, q_f, q_fT, s_f, perm_P_inv, perm_R, saved,
+                      dx, dG_P, dG_R, ws, xmem: bool = False, stream=None) -> None:
+    """The backward pass on an int8 base weight (G_P and q_f are read only
+    with xmem and may be None otherwise)."""
+    dt = _DT[sh.act]
+    m, n, b, T = sh.m, sh.n, sh.b, sh.T
+    need_ws = poetx_workspace_bytes(sh, 3 if xmem else 1)
+    need_saved = poetx_saved_bytes_xmem(sh) if xmem else poetx_saved_bytes(sh)
+    wp, wb = _ws(ws, need_ws)
+    if saved.numel() * saved.element_size() < need_saved:
+        raise ValueError(f"saved: {need_saved} bytes required")
+    check("poetx_layer_bwd_q", lib().poetx_layer_bwd_q(
+        C.byref(sh), _dev(dy, "dy", dt, T * m), _dev(G_P, "G_P", dt, n * b, optional=not xmem),
+        _dev(GT_P, "GT_P", dt, n * b), _dev(GT_R, "GT_R", dt, m * b),
+        _dev(q_f, "q_f", torch.int8, m * n, optional=not xmem),
+        _dev(q_fT, "q_fT", torch.int8, m * n), _dev(s_f, "s_f", torch.float32, m),
+        _dev(perm_P_inv, "perm_P_inv", torch.int32, n), _dev(perm_R, "perm_R", torch.int32, m),
+        _dev(saved, "saved"), _dev(dx, "dx", dt, T * n), _dev(dG_P, "dG_P", torch.float32, n * b),
+        _dev(dG_R, "dG_R", torch.float32, m * b), wp, wb, int(bool(xmem)), _stream(stream)))
 
 
 def poetx_merge(sh: Shape, W0f, G_R, GT_P, perm_R_inv, perm_P_inv, W0_out, ws,

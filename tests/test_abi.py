@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
         assert hasattr(L, s), s
         assert s in _lib.SIGNATURES, s
     assert set(_lib.SIGNATURES) == set(syms)
-    assert L.poetx_abi_version() == 1
+    assert L.poetx_abi_version() == 2
 
 
 def test_status_strings():
@@ -102,12 +102,20 @@ def test_layer_argument_errors():
     assert L.poetx_layer_fwd(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                              FAKE, need - 1, None) == 3
     need = L.poetx_workspace_bytes(C.byref(good), 1)
-    assert L.poetx_layer_bwd(C.byref(good), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
-                             FAKE, FAKE, FAKE, need - 1, None) == 3
+    bwd = lambda W0f=FAKE, W0fT=FAKE, GT_R=FAKE, ws=need: L.poetx_layer_bwd(
+        C.byref(good), FAKE, FAKE, GT_R, W0f, W0fT, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+        None)
+    assert bwd(ws=need - 1) == 3
     # null pointers are named
-    assert L.poetx_layer_bwd(C.byref(good), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
-                             FAKE, FAKE, FAKE, need, None) == 1
+    assert bwd(GT_R=None) == 1
     assert b"GT_R" in L.poetx_last_error()
+    # the backward takes the forward's W0f; its transpose is optional (the
+    # dense product then reads W0f K-major): W0f alone passes every check
+    # and stops only at the workspace
+    assert bwd(W0fT=None, ws=need - 1) == 3
+    assert bwd(W0f=None) == 1
+    assert b"W0f" in L.poetx_last_error()
+    assert bwd(W0fT=MISALIGNED) == 1
     assert L.poetx_fold_perm(0, 4, 1, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == 1
     assert L.poetx_fold_perm(4, 4, 1, FAKE, None, FAKE, FAKE, None, None, None, None) == 1
 
@@ -170,3 +178,36 @@ def test_xq_argument_errors():
     assert L.poetx_fold_scale(0, FAKE, FAKE, FAKE, None) == 1
     assert L.poetx_fold_scale(16, FAKE, None, FAKE, None) == 1
     assert L.poetx_fold_perm(4, 4, 3, FAKE, FAKE, FAKE, FAKE, None, None, None, None) == 1
+
+
+def test_int8_layer_argument_errors():
+    L = _lib.lib()
+    good = _lib.Shape(4096, 4096, 256, 4, 8192, 1)
+    need_f = L.poetx_workspace_bytes(C.byref(good), 0)
+    need_b = L.poetx_workspace_bytes(C.byref(good), 1)
+    fwd = lambda sh, qf=FAKE, sf=FAKE, ws=need_f, xmem=0: L.poetx_layer_fwd_q(
+        C.byref(sh), FAKE, FAKE, FAKE, qf, sf, FAKE, FAKE, FAKE, FAKE, FAKE, ws, xmem, None)
+    bwd = lambda sh, gp=None, qf=None, qft=FAKE, sf=FAKE, ws=need_b, xmem=0: L.poetx_layer_bwd_q(
+        C.byref(sh), FAKE, gp, FAKE, FAKE, qf, qft, sf, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+        ws, xmem, None)
+    # the int8 weight runs on bf16 MFMA kernels with whole 256-column tiles
+    assert fwd(_lib.Shape(4096, 4096, 32, 4, 64, 0)) == 2
+    assert b"bf16" in L.poetx_last_error()
+    assert fwd(_lib.Shape(4096, 4224, 128, 4, 64, 1)) == 2
+    assert fwd(_lib.Shape(4096, 4096, 32, 4, 64, 1)) == 2
+    assert fwd(good, sf=None) == 1
+    assert fwd(good, qf=None) == 1
+    assert b"q_f" in L.poetx_last_error()
+    assert fwd(good, ws=need_f - 1) == 3
+    assert fwd(good, ws=L.poetx_workspace_bytes(C.byref(good), 2) - 1, xmem=1) == 3
+    assert bwd(_lib.Shape(4096, 4096, 32, 4, 64, 0)) == 2
+    assert bwd(good, qft=None) == 1
+    assert b"q_fT" in L.poetx_last_error()
+    assert bwd(good, sf=None) == 1
+    assert bwd(good, ws=need_b - 1) == 3
+    # the memory-saving mode recomputes Z: it needs G_P and q_f
+    need_bx = L.poetx_workspace_bytes(C.byref(good), 3)
+    assert bwd(good, ws=need_bx, xmem=1) == 1
+    assert b"G_P" in L.poetx_last_error()
+    assert bwd(good, gp=FAKE, ws=need_bx, xmem=1) == 1
+    assert b"q_f" in L.poetx_last_error()

@@ -261,6 +261,38 @@ def test_repeat_runs_bitwise_equal():
         np.testing.assert_array_equal(a, bits(t))
 
 
+# ------------------------------------------------------------------ one copy of the weight
+KMAJOR_CASES = [("probe", 64, None), ("mid", 200, None), ("square", 96, None),
+                ("square", 8192, None), ("mlp_up", 64, None), ("mlp13b", 40, None),
+                ("b64_narrow", 100, I.LayerConfig("b64_narrow", 256, 192, 64, 4, 100, "bf16", 0.02))]
+
+
+@pytest.mark.parametrize("name,T,cfg", KMAJOR_CASES)
+def test_backward_reads_w0f_itself(name, T, cfg):
+    """The backward's dense product dV = dZ W0f read straight from W0f
+    (K-major: the layer holds one copy of the fixed weight) equals the read
+    from a transposed copy bit for bit, on every kernel path: the fused
+    b = 256 and b = 128 epilogues, the unfused b = 512 product, the fp32
+    and narrow-width portable kernels; the memory-saving mode likewise."""
+    cfg = cfg or I.CONFIG_BY_NAME[name]
+    say(f"K-major W0f {cfg.name} T={T}")
+    d = I.make_inputs(cfg, seed=25, T=T)
+    for xmem in (False, True):
+        outs = []
+        for keep in (True, False):
+            L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype), xmem=xmem,
+                           keep_w0ft=keep)
+            assert (L.W0fT is not None) == keep
+            L.load(to_dev(d["W0"]), to_dev(d["theta_P"]), to_dev(d["theta_R"]),
+                   to_dev(d["perm_P"]), to_dev(d["perm_R"]))
+            L.step(to_dev(d["x"]), to_dev(d["dy"]))
+            torch.cuda.synchronize()
+            outs.append([bits(t).copy() for t in (L.dx, L.dG_P, L.dG_R, L.dtheta_P, L.dtheta_R)])
+            del L
+        for a, b in zip(*outs):
+            np.testing.assert_array_equal(a, b)
+
+
 # ------------------------------------------------------------------ xmem mode
 @pytest.mark.parametrize("name,T", [("probe", 64), ("mid", 200), ("square", 96),
                                     ("mlp13b", 40), ("square", 8192), ("mlp_up", 600)])
@@ -395,9 +427,10 @@ def test_dequant_bit_exact(per_row):
     np.testing.assert_array_equal(bits(out), ref)
 
 
-def _xq_layer(cfg, d, T):
+def _xq_layer(cfg, d, T, xmem=False):
     q, sc = I.quantize_rows_int8(d["W064"])
-    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype), xq=True)
+    L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, T, act_of(cfg.dtype), xq=True, xmem=xmem)
+    assert L.W0f is None and L.W0fT is None          # no bf16 copy of the weight
     L.load_q(to_dev(q), to_dev(sc), to_dev(d["theta_P"]), to_dev(d["theta_R"]),
              to_dev(d["perm_P"]), to_dev(d["perm_R"]))
     L.step(to_dev(d["x"]), to_dev(d["dy"]))
@@ -405,10 +438,13 @@ def _xq_layer(cfg, d, T):
     return L, O.dequant_rows(q, sc)
 
 
-@pytest.mark.parametrize("name,T", [("mid", 200), ("square", 96), ("mlp13b", 40)])
+@pytest.mark.parametrize("name,T", [("mid", 200), ("square", 96), ("mlp_up", 64), ("mlp13b", 40),
+                                    ("square", 600)])
 def test_xq_layer_parity_small_T(name, T):
-    """The layer on an int8 base weight against the oracle on the weight the
-    int8 pair represents."""
+    """The layer on an int8 base weight, read by the dense kernels as int8
+    and widened in their operand path, against the oracle on the weight the
+    int8 pair represents (every workload shape; b = 128 and 256 carry the
+    block epilogue, b = 512 the separate block products)."""
     cfg = I.CONFIG_BY_NAME[name]
     say(f"xq {name} T={T}")
     d = I.make_inputs(cfg, seed=45, T=T)
@@ -418,6 +454,22 @@ def test_xq_layer_parity_small_T(name, T):
     g = O.layer_bwd(d["x64"], d["dy64"], W0q, d["theta_P64"], d["theta_R64"], d["perm_P"],
                     d["perm_R"], cfg.b, cfg.k)
     check_layer(layer_out(L), dict(g, y=y_ref), TOL[cfg.dtype], log=say)
+
+
+@pytest.mark.parametrize("name,T", [("square", 96), ("mid", 200), ("mlp13b", 40)])
+def test_xq_xmem_bitwise_equals_xq(name, T):
+    """The memory-saving mode on the int8 weight recomputes Z with the
+    forward's own int8 kernel: every output equals the default mode's."""
+    cfg = I.CONFIG_BY_NAME[name]
+    say(f"xq xmem {name} T={T}")
+    d = I.make_inputs(cfg, seed=47, T=T)
+    outs = []
+    for xmem in (False, True):
+        L, _ = _xq_layer(cfg, d, T, xmem=xmem)
+        outs.append([bits(t).copy() for t in (L.y, L.dx, L.dG_P, L.dG_R, L.dtheta_P, L.dtheta_R)])
+        del L
+    for a, b in zip(*outs):
+        np.testing.assert_array_equal(a, b)
 
 
 def test_xq_layer_full_size():
