@@ -447,6 +447,295 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   }
 }
 
+// Blocks of 512: 128-column panels (four per block), eight waves of 64 rows
+// x 128 columns.  Q (512 KB in bf16) does not fit LDS and is read straight
+// from L2 as the MFMA A operand in fragment order (q_off), so what bounds a
+// Horner step is the L2-to-CU traffic of Q: a panel streams all of Q once
+// per step, and four panels per block instead of sixteen cut that traffic
+// to a quarter: each Q fragment now feeds four MFMAs.  The panel X^T
+// (128 x 512 bf16) is the B operand in LDS.
+// Each step's addend is loaded at the start of the step straight into the
+// accumulators (the MFMAs then add the product to it), so its L2 latency is
+// paid once per step, for all eight tiles of a wave together:
+//   forward  X_s = c Q[:, panel] + Q X_{s+1};  Q[row][J0 + c] = -Q[J0 + c][row]
+//            gives four consecutive rows of a lane as one 8-byte piece of
+//            row J0 + c of Q in fragment order;
+//   phase 1  X_s = F_s^T = w_{s+1} D^T - Q X_{s+1} (the product with -Q: the
+//            A fragments' sign bits flipped); four consecutive rows of a lane
+//            are one 16-byte piece of row J0 + c of D.  The panel of F_s is
+//            stored (bf16) from its LDS copy, whose rows are rows of F_s;
+//   phase 2  Y_s = F_s + Q Y_{s+1}, Y_k = w_{k+1} D: 32 lanes read 32
+//            consecutive columns of a row.
+// Phase 2 reads the bf16 F_s itself, where the narrower panels keep
+// F_s - w D (a smaller quantity) in bf16; the rounding of that one term is
+// the only difference in arithmetic.
+__device__ __forceinline__ void wide_tile(int id, int nwg, int npan, int& blk, int& pan) {
+  // workgroups are dealt round-robin over the 8 XCDs: give each XCD a
+  // contiguous range of (block, panel) pairs, so a block's panels share an
+  // XCD and its L2 copy of Q (any workgroup count)
+  const int x = id % 8, s = id / 8, full = nwg / 8, rem = nwg % 8;
+  const int L = x * full + min(x, rem) + s;
+  blk = L / npan;
+  pan = L % npan;
+}
+
+// One panel of 32 * CTW columns of block blk; Xs is [32 * CTW][QP].
+template <int MODE, int CTW>
+__device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
+                                          const bf16* __restrict__ Qg, const float* __restrict__ D,
+                                          bf16* __restrict__ out_bf, bf16* __restrict__ out_bfT,
+                                          float* __restrict__ out_f, bf16* __restrict__ Xs) {
+  constexpr int B = 512, PWW = 32 * CTW, QP = B + PAD;
+  constexpr int RTW = 2;       // row tiles per wave (eight waves: all 512 rows)
+  constexpr int NKS = B / 16;  // K-steps of one product
+  // Phase 1 keeps its panel of D^T in registers (read once, not once per
+  // step): a second accumulator-sized register set, so panels of at most 64.
+  constexpr bool DRES = MODE == MODE_BWD1;
+  static_assert(!DRES || CTW <= 2, "register budget");
+  const int J0 = pan * PWW;
+  const int lane = threadIdx.x % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: scalar offsets
+  const int col = lane % 32, h = lane / 32;
+  const long boff = (long)blk * B * B;
+  const bf16* Qb = Qg + boff;
+  f32x16_t P[RTW][CTW];
+  float Dr[DRES ? RTW : 1][DRES ? CTW : 1][DRES ? 16 : 1];
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  // The addends are read through buffer resources over one block: a lane's
+  // offset is one 32-bit register per column tile, the rest a wave-uniform
+  // constant, so no 64-bit address per element stays live.
+  const __amdgpu_buffer_rsrc_t rsQ =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Qb, (short)0, B * B * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(D ? D + boff : nullptr), (short)0, D ? B * B * 4 : 0, 0x00020000);
+
+  // P = the addend of step s (s = k: the starting X), every tile at once
+  auto load_addend = [&](int s) {
+    const float w = (MODE == MODE_FWD) ? (s == k ? 1.f : cnp_coef(s + 1, k)) : cnp_wcoef(s + 1, k);
+    if constexpr (DRES) {
+      if (s < k) {
+#pragma unroll
+        for (int t = 0; t < RTW; ++t)
+#pragma unroll
+          for (int u = 0; u < CTW; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) P[t][u][r] = w * Dr[t][u][r];
+        return;
+      }
+    }
+    int c0 = J0 + col, hh = h;
+    asm volatile("" : "+v"(c0), "+v"(hh));  // recomputed per step, not kept
+    __amdgpu_buffer_rsrc_t rsF = rsD;
+    if constexpr (MODE == MODE_BWD2) {
+      if (s < k)
+        rsF = __builtin_amdgcn_make_buffer_rsrc((void*)(out_bf + ((long)s * nblk + blk) * B * B),
+                                               (short)0, B * B * 2, 0x00020000);
+    }
+#pragma unroll
+    for (int u = 0; u < CTW; ++u) {
+      const int c = c0 + u * 32;
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) {
+        const int rt = wave * RTW + t;
+        if constexpr (MODE == MODE_FWD) {
+          // Q[row][c] = -Q[c][row]: rows rt*32 + 8q + 4h .. +3 of column c
+          // are one 8-byte piece of row c in fragment order
+          const int lo = (int)q_off(c, 4 * hh, B, true) * 2;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int so = (int)(q_off(rt * 32, rt * 32 + 8 * q, B, true) - q_off(rt * 32, rt * 32, B, true)) * 2 +
+                           (rt * 2) * 1024;
+            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rsQ, lo, so, 0);
+            P[t][u][4 * q + 0] = -w * __uint_as_float(v.x << 16);
+            P[t][u][4 * q + 1] = -w * __uint_as_float(v.x & 0xffff0000u);
+            P[t][u][4 * q + 2] = -w * __uint_as_float(v.y << 16);
+            P[t][u][4 * q + 3] = -w * __uint_as_float(v.y & 0xffff0000u);
+          }
+        } else if constexpr (MODE == MODE_BWD1) {
+          // D^T[row][c] = D[c][row]: four consecutive rows are 16 bytes of row c
+          const int lo = (c * B + 4 * hh) * 4;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rsD, lo, (rt * 32 + 8 * q) * 4, 0);
+            Dr[t][u][4 * q + 0] = __uint_as_float(v.x);
+            Dr[t][u][4 * q + 1] = __uint_as_float(v.y);
+            Dr[t][u][4 * q + 2] = __uint_as_float(v.z);
+            Dr[t][u][4 * q + 3] = __uint_as_float(v.w);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) P[t][u][r] = w * Dr[t][u][r];
+        } else if (s < k) {
+          // F_s[row][c], row = rt*32 + 8(r/4) + 4h + r%4
+          const int lo = (4 * hh * B + c) * 2;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(
+                rsF, lo, (rt * 32 + 8 * (r / 4) + r % 4) * B * 2, 0);
+            P[t][u][r] = bf2f((bf16)v);
+          }
+        } else {
+          // s = k: Y_k = w D
+          const int lo = (4 * hh * B + c) * 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            P[t][u][r] = w * __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                                 rsD, lo, (rt * 32 + 8 * (r / 4) + r % 4) * B * 4, 0));
+        }
+      }
+    }
+  };
+  // P (bf16) into Xs as X^T: rows r, r+1 of a lane's column are one 4-byte word
+  auto store_x = [&]() {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+#pragma unroll
+      for (int u = 0; u < CTW; ++u) {
+        const int rt = wave * RTW + t, c = u * 32 + col;
+#pragma unroll
+        for (int r = 0; r < 16; r += 2)
+          *reinterpret_cast<uint32_t*>(Xs + c * QP + rt * 32 + acc_row(r, lane)) =
+              pack2bf(P[t][u][r], P[t][u][r + 1]);
+      }
+  };
+  // phase 1: rows J0 .. J0 + PWW - 1 of F_s from Xs, 16-byte stores
+  auto store_f = [&](int s) {
+    bf16* F = out_bf + ((long)s * nblk + blk) * B * B;
+    constexpr int VPR = B / 8;  // 16-byte vectors per row
+#pragma unroll
+    for (int v = threadIdx.x; v < PWW * VPR; v += 512) {
+      const int r = v / VPR, c8 = (v % VPR) * 8;
+      *reinterpret_cast<uint4*>(F + (long)(J0 + r) * B + c8) = *reinterpret_cast<const uint4*>(Xs + r * QP + c8);
+    }
+  };
+
+  load_addend(k);
+  // one offset per row tile (its K-step 0 fragment; K-step ks lies ks KB
+  // further), passed through an empty asm each step so that the compiler
+  // does not hoist the wave's Q loads out of the step loop
+  int qoff[RTW];
+#pragma unroll
+  for (int t = 0; t < RTW; ++t) qoff[t] = (int)q_off((wave * RTW + t) * 32 + col, 8 * h, B, true);
+  // phase 1 multiplies by -Q: flip the sign bits of its bf16 fragments
+  const uint32_t qsign = (MODE == MODE_BWD1) ? 0x80008000u : 0u;
+
+  for (int s = k - 1; s >= 0; --s) {
+    store_x();
+    __syncthreads();
+    load_addend(s);
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) asm volatile("" : "+v"(qoff[t]));
+    {
+      // P += (+-Q) X: Q fragments from L2 two K-steps ahead, X fragments
+      // from LDS one K-step ahead
+      constexpr int QPF = 2;
+      uint4 aq[QPF][RTW], bq[2][CTW];
+      auto fetch_a = [&](int ks, int sl) {
+#pragma unroll
+        for (int t = 0; t < RTW; ++t) {
+          uint4 v = *reinterpret_cast<const uint4*>(Qb + qoff[t] + ks * 512);
+          v.x ^= qsign;
+          v.y ^= qsign;
+          v.z ^= qsign;
+          v.w ^= qsign;
+          aq[sl][t] = v;
+        }
+      };
+      auto fetch_b = [&](int ks, int sl) {
+#pragma unroll
+        for (int u = 0; u < CTW; ++u)
+          bq[sl][u] = *reinterpret_cast<const uint4*>(Xs + (u * 32 + col) * QP + ks * 16 + 8 * h);
+      };
+#pragma unroll
+      for (int i = 0; i < QPF; ++i) fetch_a(i, i);
+      fetch_b(0, 0);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        if (ks + 1 < NKS) fetch_b(ks + 1, (ks + 1) & 1);
+#pragma unroll
+        for (int t = 0; t < RTW; ++t)
+#pragma unroll
+          for (int u = 0; u < CTW; ++u)
+            P[t][u] = mfma32x32x16(as_bf16x8(aq[ks % QPF][t]), as_bf16x8(bq[ks & 1][u]), P[t][u]);
+        if (ks + QPF < NKS) fetch_a(ks + QPF, ks % QPF);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // phase 1: F_{s+1} (this step's B operand, in Xs; F_k = w D is not
+    // stored) goes out after the step's last Q loads, so that no Q load
+    // waits behind these stores
+    if constexpr (MODE == MODE_BWD1) {
+      if (s + 1 < k) store_f(s + 1);
+    }
+    __syncthreads();  // every wave finished reading Xs
+  }
+
+  // outputs: G = I + X_0 and G^T (forward), F_0 (phase 1), dQ = Y_0 (phase 2)
+  if constexpr (MODE == MODE_FWD) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+#pragma unroll
+      for (int u = 0; u < CTW; ++u) {
+        const int rt = wave * RTW + t, c = J0 + u * 32 + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rt * 32 + acc_row(r, lane);
+          P[t][u][r] += (row == c) ? 1.f : 0.f;
+          out_bf[boff + (long)row * B + c] = f2bf(P[t][u][r]);
+        }
+      }
+    if (out_bfT) {  // rows J0 .. J0 + PWW - 1 of G^T, through Xs
+      store_x();
+      __syncthreads();
+      bf16* GT = out_bfT + boff;
+      constexpr int VPR = B / 8;
+#pragma unroll
+      for (int v = threadIdx.x; v < PWW * VPR; v += 512) {
+        const int r = v / VPR, c8 = (v % VPR) * 8;
+        *reinterpret_cast<uint4*>(GT + (long)(J0 + r) * B + c8) = *reinterpret_cast<const uint4*>(Xs + r * QP + c8);
+      }
+    }
+  } else if constexpr (MODE == MODE_BWD1) {
+    store_x();
+    __syncthreads();
+    store_f(0);
+  } else {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t)
+#pragma unroll
+      for (int u = 0; u < CTW; ++u) {
+        const int rt = wave * RTW + t, c = J0 + u * 32 + col;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) out_f[boff + (long)(rt * 32 + acc_row(r, lane)) * B + c] = P[t][u][r];
+      }
+  }
+}
+
+// Workgroups 0 .. 4 nmain - 1 take blocks 0 .. nmain - 1 in 32 * CTM-column
+// panels; the rest take the remaining blocks in 32 * CTT-column panels.  A
+// block count that leaves a partial last round of 128-column panels (74
+// blocks: 296 panels on 256 CUs) would otherwise run two full panel times;
+// the narrower tail panels fill that round in a fraction of one.
+template <int MODE, int CTM, int CTT>
+__global__ __launch_bounds__(512, 1) void k_cnp_wide(int k, int nmain, int nblk,
+                                                     const bf16* __restrict__ Qg,
+                                                     const float* __restrict__ D,
+                                                     bf16* __restrict__ out_bf,
+                                                     bf16* __restrict__ out_bfT,
+                                                     float* __restrict__ out_f) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* Xs = reinterpret_cast<bf16*>(smem);
+  const int id = blockIdx.x, wm = (16 / CTM) * nmain;
+  int blk, pan;
+  if (CTM != CTT && id < wm) {
+    wide_tile(id, wm, 16 / CTM, blk, pan);
+    wide_body<MODE, CTM>(k, blk, pan, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
+  } else {
+    wide_tile(id - wm, (int)gridDim.x - wm, 16 / CTT, blk, pan);
+    wide_body<MODE, CTT>(k, nmain + blk, pan, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
+  }
+}
+
 // dtheta[t(i,j)] (+)= gQ[i][j] - gQ[j][i], one workgroup per (row i, block)
 // dtheta(i, j) = dQ[i][j] - dQ[j][i] for i < j (set or accumulate).  One
 // workgroup per tile pair (I, J): tiles (I, J) and (J, I) of dQ are read with
@@ -503,6 +792,57 @@ hipError_t launch_panel(int nblk, int k, const float* theta, const bf16* Qg, con
   return hipGetLastError();
 }
 
+int cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+// Blocks given 128-column panels (the rest get 64-column ones): the split
+// with the fewest panel times, counting a 64-column panel as 0.55 of a
+// 128-column one (it streams all of Q per step for half the columns) and
+// one panel per CU at a time.
+int wide_split(int nblk, int ncu) {
+  auto rounds = [&](long wg) { return (double)((wg + ncu - 1) / ncu); };
+  int best = nblk;
+  double tbest = rounds(4L * nblk);
+  for (int r = 0; (long)r * ncu <= 4L * nblk; ++r) {
+    const int M = (int)((long)r * ncu / 4);
+    if (M > nblk) break;
+    const double t = rounds(4L * M) + 0.55 * rounds(8L * (nblk - M));
+    if (t < tbest - 1e-9) {
+      tbest = t;
+      best = M;
+    }
+  }
+  return best;
+}
+
+template <int MODE>
+hipError_t launch_wide(int nblk, int k, const bf16* Qg, const float* D, bf16* out_bf,
+                       bf16* out_bfT, float* out_f, hipStream_t s) {
+  // the forward and phase 2 take 128-column panels where they fill whole
+  // rounds of the CUs; phase 1 takes 64-column panels throughout
+  constexpr int CTM = MODE == MODE_BWD1 ? 2 : 4, CTT = 2;
+  constexpr size_t lds = (size_t)32 * CTM * (512 + PAD) * sizeof(bf16);
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  auto kern = k_cnp_wide<MODE, CTM, CTT>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
+  const int nmain = CTM == CTT ? 0 : wide_split(nblk, cu_count());
+  const long nwg = (long)(16 / CTM) * nmain + (long)(16 / CTT) * (nblk - nmain);
+  hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(512), lds, s, k, nmain, nblk, Qg, D, out_bf,
+                     out_bfT, out_f);
+  return hipGetLastError();
+}
+
 template <int MODE>
 hipError_t dispatch_panel(int nblk, int b, int k, const float* theta, const bf16* Qg,
                           const float* D, bf16* out_bf, bf16* out_bfT, float* out_f,
@@ -511,7 +851,7 @@ hipError_t dispatch_panel(int nblk, int b, int k, const float* theta, const bf16
     case 64: return launch_panel<64, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
     case 128: return launch_panel<128, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
     case 256: return launch_panel<256, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
-    case 512: return launch_panel<512, MODE>(nblk, k, theta, Qg, D, out_bf, out_bfT, out_f, s);
+    case 512: return launch_wide<MODE>(nblk, k, Qg, D, out_bf, out_bfT, out_f, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -726,10 +726,18 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 }
 
 
+// vmcnt(N), optionally with lgkmcnt(0), as an s_waitcnt immediate (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+template <int N, bool LGKM0>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | ((LGKM0 ? 0 : 15) << 8) | ((N >> 4) << 14));
+}
+
 // Token reduction P[s][bt][r][c] = sum over split s's tokens of
-// A[t][bt*sA + tr*TILE + r] * B[t][bt*sB + tc*TILE + c]  (dG = dS^T Z, dV^T U).
+// A[t][bt*sA + tr*TM + r] * B[t][bt*sB + tc*TN + c]  (dG = dS^T Z, dV^T U).
 // A 4-wave, DMA-fed MFMA pipeline like k_nt4's (hand-fixed issue order, vmcnt
-// counted by hand), here with K slabs of 32 tokens in four 32 KB stages and
+// counted by hand), here with K slabs of 32 tokens in four LDS stages and
 // the operands' roles transposed: both operands are token-major, so a K
 // slab lands in LDS as [token][feature]
 // rows (buffer_load ... lds: rows past the split's end read as zero), and
@@ -738,52 +746,66 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 // tile.  Two transposed reads give the eight consecutive tokens (K values) a
 // lane holds.  The 16-byte chunk index of a token row is XORed with
 // 2 * (token % 4), so the four rows one read touches fall on distinct banks.
-// Output: an fp32 TILE x TILE partial, staged through LDS for 16-byte stores.
+// Output: an fp32 TM x TN partial, staged through LDS for 16-byte stores.
+// A TM x TN tile of a D x D product: TN = TM / 2 gives twice the
+// workgroups of square tiles for the same token splits (and fp32
+// partials); the two column halves of a tile read the same A slabs, and the
+// renumbering below puts them on one XCD, so that A comes from its L2.
 // One launch can serve two operand pairs of the same D (dG_R and dG_P):
 // batch entries below nb0 read (A0, B0), the rest (A1, B1).  With one token
 // split and P1 set, the second pair writes its sums to P1 instead of after
 // the first pair's in P (two output buffers, no reduction pass).
-template <int TILE>
+template <int TM, int TN, int NSTG>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_tn4(
-    int T, int tsplit, int tiles1, const bf16* __restrict__ A0, long lda0, long sA,
-    const bf16* __restrict__ B0, long ldb0, long sB, float* __restrict__ P, long ldp, long sP,
-    long sS, int nb0, const bf16* __restrict__ A1, long lda1, const bf16* __restrict__ B1,
+    int T, int tsplit, int tilesN, int ntiles, int nbatch, const bf16* __restrict__ A0, long lda0,
+    long sA, const bf16* __restrict__ B0, long ldb0, long sB, float* __restrict__ P, long ldp,
+    long sP, long sS, int nb0, const bf16* __restrict__ A1, long lda1, const bf16* __restrict__ B1,
     long ldb1, float* __restrict__ P1) {
-  constexpr int WT = TILE / 2, FM = WT / 32, FN = WT / 32, NF = FM + FN;
-  constexpr int MPG = FM * FN / NF;               // MFMAs per group
-  constexpr int ROWB_T = TILE * 2;                // LDS bytes per token row
-  constexpr int A_BYTES = 32 * ROWB_T, STG = 2 * A_BYTES, NSTG = 4;
+  constexpr int WTM = TM / 2, WTN = TN / 2, FM = WTM / 32, FN = WTN / 32, NF = FM + FN;
+  constexpr int NMMA = FM * FN;                   // MFMAs per K-step, spread over NF groups
+  constexpr int ROWA = TM * 2, ROWB = TN * 2;     // LDS bytes per token row
+  constexpr int A_BYTES = 32 * ROWA, STG = A_BYTES + 32 * ROWB;
   constexpr int NQ = STG / 1024 / 4;              // DMA instructions per wave per slab
   static_assert(NQ == NF, "one DMA per group");
   extern __shared__ __align__(16) char smem[];
   const int tid = threadIdx.x, lane = tid % 64, wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
-  const int tr = blockIdx.x / tiles1, tc = blockIdx.x % tiles1;
+  // workgroups are dealt round-robin over the 8 XCDs: number them so each
+  // XCD takes a contiguous range of (tile, batch, split), tiles fastest
+  int L;
+  {
+    const int nwg = gridDim.x;
+    const int x = blockIdx.x % 8, q = blockIdx.x / 8, full = nwg / 8, rem = nwg % 8;
+    L = x * full + min(x, rem) + q;
+  }
+  const int tile = L % ntiles, by = (L / ntiles) % nbatch, s = L / (ntiles * nbatch);
+  const int tr = tile / tilesN, tc = tile % tilesN;
   // batch entries from nb0 on belong to the second operand pair (A1, B1);
   // the partials are indexed over both
-  const bool second = (int)blockIdx.y >= nb0;
-  const long bt = second ? (long)blockIdx.y - nb0 : (long)blockIdx.y;
+  const bool second = by >= nb0;
+  const long bt = second ? (long)by - nb0 : (long)by;
   const bf16* __restrict__ A = second ? A1 : A0;
   const bf16* __restrict__ B = second ? B1 : B0;
   const long lda = second ? lda1 : lda0, ldb = second ? ldb1 : ldb0;
-  const int s = blockIdx.z;
   const int t_begin = s * tsplit, t_end = min(T, t_begin + tsplit);
   // P1 set: one token split, each pair straight into its own output
-  P = P1 && second ? P1 + bt * sP : P + s * sS + (long)blockIdx.y * sP;
+  P = P1 && second ? P1 + bt * sP : P + s * sS + (long)by * sP;
   const int ntok = max(0, t_end - t_begin);
   const int nk = max(1, (ntok + 31) / 32);
   const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
   const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + (long)t_begin * lda + bt * sA + tr * TILE), (short)0, ntok * (int)lda * 2, 0x00020000);
+      (void*)(A + (long)t_begin * lda + bt * sA + tr * TM), (short)0, ntok * (int)lda * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(B + (long)t_begin * ldb + bt * sB + tc * TILE), (short)0, ntok * (int)ldb * 2, 0x00020000);
+      (void*)(B + (long)t_begin * ldb + bt * sB + tc * TN), (short)0, ntok * (int)ldb * 2, 0x00020000);
   int vo[NQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
     const int off = (q * 4 + wave) * 1024 + 16 * lane;
-    const int o = off % A_BYTES, row = o / ROWB_T, pc = (o % ROWB_T) / 16;
+    const bool isA = off < A_BYTES;
+    const int o = isA ? off : off - A_BYTES, rb = isA ? ROWA : ROWB;
+    const int row = o / rb, pc = (o % rb) / 16;
     const int lc = pc ^ ((row & 3) << 1);
-    vo[q] = off < A_BYTES ? row * (int)lda * 2 + lc * 16 : row * (int)ldb * 2 + lc * 16;
+    vo[q] = row * (int)(isA ? lda : ldb) * 2 + lc * 16;
   }
   const int slabA = 32 * (int)lda * 2, slabB = 32 * (int)ldb * 2;
 #define DMA1(slot, from, q)                                                                   \
@@ -802,16 +824,17 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #define FRAG(F, slab, ks, g)                                                                  \
   {                                                                                           \
     const char* S_ = smem + ((slab) % NSTG) * STG + ((g) < FM ? 0 : A_BYTES);                 \
-    const int ft_ = ((g) < FM ? wm * WT + (g) * 32 : wn * WT + ((g) - FM) * 32) + ft_l;        \
+    const int rb_ = (g) < FM ? ROWA : ROWB;                                                   \
+    const int ft_ = ((g) < FM ? wm * WTM + (g) * 32 : wn * WTN + ((g) - FM) * 32) + ft_l;      \
     const int t0_ = 16 * (ks) + tk_l, t1_ = t0_ + 4;                                           \
-    const char* p0_ = S_ + t0_ * ROWB_T + (((ft_ >> 3) ^ ((t0_ & 3) << 1)) << 4) + (ft_ & 7) * 2; \
-    const char* p1_ = S_ + t1_ * ROWB_T + (((ft_ >> 3) ^ ((t1_ & 3) << 1)) << 4) + (ft_ & 7) * 2; \
+    const char* p0_ = S_ + t0_ * rb_ + (((ft_ >> 3) ^ ((t0_ & 3) << 1)) << 4) + (ft_ & 7) * 2;  \
+    const char* p1_ = S_ + t1_ * rb_ + (((ft_ >> 3) ^ ((t1_ & 3) << 1)) << 4) + (ft_ & 7) * 2;  \
     if ((g) < FM) fa[F][(g)] = frag_tr(p0_, p1_);                                             \
     else fb[F][(g) - FM] = frag_tr(p0_, p1_);                                                 \
   }
+  // group g issues MFMAs g NMMA / NF .. (g + 1) NMMA / NF - 1 of the K-step
 #define MMAG(F, g)                                                                            \
-  _Pragma("unroll") for (int u_ = 0; u_ < MPG; ++u_) {                                        \
-    const int m_ = (g) * MPG + u_;                                                            \
+  _Pragma("unroll") for (int m_ = (g) * NMMA / NF; m_ < ((g) + 1) * NMMA / NF; ++m_) {         \
     acc[m_ / FN][m_ % FN] = mfma32x32x16(fa[F][m_ / FN], fb[F][m_ % FN], acc[m_ / FN][m_ % FN]); \
   }
   f32x16_t acc[FM][FN];
@@ -824,8 +847,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   for (int p = 0; p < NSTG; ++p)
 #pragma unroll
     for (int q = 0; q < NQ; ++q) DMA1(p, min(p, nk - 1), q);
-  if constexpr (NQ == 8) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  wait_vm<(NSTG - 1) * NQ, false>();  // stage 0 has landed
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < NF; ++g) FRAG(0, 0, 0, g);
@@ -836,8 +858,8 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
       MMAG(0, g);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (NQ == 8) asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+    // stage kt + 1 has landed; this wave's reads of stage kt are complete
+    wait_vm<(NSTG - 2) * NQ, true>();
     __syncthreads();
     const int refill = min(kt + NSTG, nk - 1);
 #pragma unroll
@@ -853,32 +875,34 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
 #undef MMAG
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  // fp32 tile out through LDS in passes of PR rows: [row][TILE] with the
+  // fp32 tile out through LDS in passes of PR rows: [row][TN] with the
   // 16-byte chunk index XOR (row & 7), then 16-byte row stores
-  constexpr int PR = (NSTG * STG) / (TILE * 4) < TILE ? (NSTG * STG) / (TILE * 4) : TILE;
+  constexpr int PR0 = (NSTG * STG) / (TN * 4);
+  constexpr int PR = PR0 >= TM ? TM : (PR0 >= 128 ? 128 : 64);
+  static_assert(TM % PR == 0 && PR * TN * 4 <= NSTG * STG, "output passes");
   float* st = reinterpret_cast<float*>(smem);
 #pragma unroll
-  for (int pass = 0; pass < TILE / PR; ++pass) {
+  for (int pass = 0; pass < TM / PR; ++pass) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int rb = wm * WT + i * 32;
+      const int rb = wm * WTM + i * 32;
       if (rb < pass * PR || rb >= (pass + 1) * PR) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = rb - pass * PR + acc_row(r, lane);
-          const int col = wn * WT + j * 32 + lane % 32;
-          st[row * TILE + (((col >> 2) ^ (row & 7)) << 2) + (col & 3)] = acc[i][j][r];
+          const int col = wn * WTN + j * 32 + lane % 32;
+          st[row * TN + (((col >> 2) ^ (row & 7)) << 2) + (col & 3)] = acc[i][j][r];
         }
     }
     __syncthreads();
-    constexpr int CH = PR * TILE / 4;  // 16-byte chunks in the pass
+    constexpr int CH = PR * TN / 4;  // 16-byte chunks in the pass
 #pragma unroll
     for (int u = 0; u < CH / 256; ++u) {
-      const int q = u * 256 + tid, row = q / (TILE / 4), c4 = q % (TILE / 4);
-      const float4 v = *reinterpret_cast<const float4*>(st + row * TILE + ((c4 ^ (row & 7)) << 2));
-      *reinterpret_cast<float4*>(P + (long)(tr * TILE + pass * PR + row) * ldp + tc * TILE + c4 * 4) = v;
+      const int q = u * 256 + tid, row = q / (TN / 4), c4 = q % (TN / 4);
+      const float4 v = *reinterpret_cast<const float4*>(st + row * TN + ((c4 ^ (row & 7)) << 2));
+      *reinterpret_cast<float4*>(P + (long)(tr * TM + pass * PR + row) * ldp + tc * TN + c4 * 4) = v;
     }
     __syncthreads();
   }
@@ -1303,15 +1327,27 @@ hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, 
   return hipErrorInvalidValue;
 }
 
+// Tile width of the D >= 256 reduction (k_tn4): 256 x 128 tiles, twice the
+// workgroups of 256 x 256 ones, while that keeps the launch within one
+// round of the CUs; then as many token splits as fill the CUs.
+int tn4_width(int batch, int D) {
+  const long tiles256 = (long)batch * (D / 256) * (D / 256);
+  return 2 * tiles256 <= NUM_CU ? 128 : 256;
+}
+
 // splits of the token range for a D x D (per batch) reduction whose widest
 // operand has row pitch `width` (elements)
 int tn_splits(int batch, int D, int T, long width) {
-  const int BT = D >= 256 ? 256 : (D >= 128 ? 128 : 64);
-  const long tiles = (long)batch * (D / BT) * (D / BT);
-  // D >= 256 (k_tn4): half the CUs already saturate HBM there, and fewer
-  // splits mean fewer fp32 partials to write and reduce
-  const long want = D >= 256 ? NUM_CU / 2 : NUM_CU;
-  int S = (int)((want + tiles - 1) / tiles);
+  int S;
+  if (D >= 256) {
+    // k_tn4: fill the CUs once; more splits only add fp32 partials
+    const long tiles = (long)batch * (D / 256) * (D / tn4_width(batch, D));
+    S = (int)std::max<long>(1, NUM_CU / tiles);
+  } else {
+    const int BT = D >= 128 ? 128 : 64;
+    const long tiles = (long)batch * (D / BT) * (D / BT);
+    S = (int)((NUM_CU + tiles - 1) / tiles);
+  }
   const int max_s = (T + 255) / 256;  // keep >= 256 tokens per split
   S = S < max_s ? S : max_s;
   if (S < 1) S = 1;
@@ -1332,25 +1368,42 @@ size_t tn_partial_bytes(int batch, int D, int T, long width) {
 
 namespace {
 
-// k_tn4 over `batch` D x D products (D a multiple of 256) in S token splits;
-// entries from nb0 on read (A1, B1).  Writes P[s][batch][D][D].
-hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, long lda0,
-                      const bf16* B0, long ldb0, const bf16* A1, long lda1, const bf16* B1,
-                      long ldb1, float* P, hipStream_t s, float* P1 = nullptr) {
-  constexpr int lds = 4 * 2 * 32 * 256 * 2;  // four stages of 32 tokens x (A, B) rows
-  static const hipError_t attr = set_lds(k_tn4<256>, lds);
+#ifndef POETX_TN128_STAGES
+#define POETX_TN128_STAGES 4
+#endif
+#ifndef POETX_TN256_STAGES
+#define POETX_TN256_STAGES 4
+#endif
+template <int TN>
+hipError_t tn4_launch_w(int batch, int nb0, int D, int T, int S, const bf16* A0, long lda0,
+                        const bf16* B0, long ldb0, const bf16* A1, long lda1, const bf16* B1,
+                        long ldb1, float* P, hipStream_t s, float* P1) {
+  constexpr int NSTG = TN == 128 ? POETX_TN128_STAGES : POETX_TN256_STAGES;
+  constexpr int lds = NSTG * 32 * (256 + TN) * 2;  // stages of 32 tokens x (A, B) rows
+  static_assert(lds <= 160 * 1024, "LDS budget");
+  static const hipError_t attr = set_lds(k_tn4<256, TN, NSTG>, lds);
   if (attr != hipSuccess) return attr;
   const long dd = (long)D * D;
-  const int tiles1 = D / 256;
+  const int tilesN = D / TN, ntiles = (D / 256) * tilesN;
   const int tsplit = ((T + S - 1) / S + 31) / 32 * 32;
   // a split's buffer range (tsplit rows of the widest operand) stays below
   // 2^31 bytes; tn_splits chose S for that, this only guards the invariant
   if ((long)tsplit * std::max(std::max(lda0, ldb0), std::max(lda1, ldb1)) * 2 >= (1L << 31))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_tn4<256>, dim3(tiles1 * tiles1, batch, S), dim3(256), lds, s, T, tsplit,
-                     tiles1, A0, lda0, (long)D, B0, ldb0, (long)D, P, (long)D, dd, dd * batch, nb0,
-                     A1, lda1, B1, ldb1, P1);
+  hipLaunchKernelGGL((k_tn4<256, TN, NSTG>), dim3(ntiles * batch * S), dim3(256), lds, s, T, tsplit,
+                     tilesN, ntiles, batch, A0, lda0, (long)D, B0, ldb0, (long)D, P, (long)D, dd,
+                     dd * batch, nb0, A1, lda1, B1, ldb1, P1);
   return hipGetLastError();
+}
+
+// k_tn4 over `batch` D x D products (D a multiple of 256) in S token splits;
+// entries from nb0 on read (A1, B1).  Writes P[s][batch][D][D].
+hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, long lda0,
+                      const bf16* B0, long ldb0, const bf16* A1, long lda1, const bf16* B1,
+                      long ldb1, float* P, hipStream_t s, float* P1 = nullptr) {
+  if (tn4_width(batch, D) == 128)
+    return tn4_launch_w<128>(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, P, s, P1);
+  return tn4_launch_w<256>(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, P, s, P1);
 }
 
 // out0 = the first n0 sums over S partials of stride n, out1 = the rest

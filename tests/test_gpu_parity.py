@@ -66,6 +66,8 @@ CNP_CASES = [  # nblk, b, k, dtype, sigma
     (5, 256, 2, "bf16", 0.01),
     (3, 512, 5, "bf16", 0.005),
     (37, 512, 5, "bf16", 0.005),
+    (74, 512, 5, "bf16", 0.005),   # 128-column panels for 64 blocks, 64-column ones for 10
+    (65, 512, 3, "bf16", 0.005),   # the same split with a single 64-column block
     (2, 512, 0, "bf16", 0.005),
     (2, 512, 1, "bf16", 0.005),
 ]
