@@ -539,19 +539,8 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
       for (int t = 0; t < RTW; ++t) {
         const int rt = wave * RTW + t;
         if constexpr (MODE == MODE_FWD) {
-          // Q[row][c] = -Q[c][row]: rows rt*32 + 8q + 4h .. +3 of column c
-          // are one 8-byte piece of row c in fragment order
-          const int lo = (int)q_off(c, 4 * hh, B, true) * 2;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int so = (int)(q_off(rt * 32, rt * 32 + 8 * q, B, true) - q_off(rt * 32, rt * 32, B, true)) * 2 +
-                           (rt * 2) * 1024;
-            const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rsQ, lo, so, 0);
-            P[t][u][4 * q + 0] = -w * __uint_as_float(v.x << 16);
-            P[t][u][4 * q + 1] = -w * __uint_as_float(v.x & 0xffff0000u);
-            P[t][u][4 * q + 2] = -w * __uint_as_float(v.y << 16);
-            P[t][u][4 * q + 3] = -w * __uint_as_float(v.y & 0xffff0000u);
-          }
+          // the c Q[:, panel] term enters through the products (below)
+          P[t][u] = (f32x16_t){};
         } else if constexpr (MODE == MODE_BWD1) {
           // D^T[row][c] = D[c][row]: four consecutive rows are 16 bytes of row c
           const int lo = (c * B + 4 * hh) * 4;
@@ -618,6 +607,48 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
   for (int t = 0; t < RTW; ++t) qoff[t] = (int)q_off((wave * RTW + t) * 32 + col, 8 * h, B, true);
   // phase 1 multiplies by -Q: flip the sign bits of its bf16 fragments
   const uint32_t qsign = (MODE == MODE_BWD1) ? 0x80008000u : 0u;
+  // The forward's addend c Q[:, panel] = Q (c E_panel) is a product too:
+  // after the step's own K-steps come 2 CTW more over K = the panel's
+  // columns, each row tile taking one product with c times an identity
+  // block as the B fragment.  Exact (c is 1 or 2, Q is bf16), and no load
+  // of the addend stands before the step's first product.
+  constexpr int NID = MODE == MODE_FWD ? 2 * CTW : 0;  // identity K-steps
+  const int kb = J0 / 16;                              // the panel's first K-step
+  // lane (col, h) of the identity fragment of panel K-step m has its one
+  // nonzero at element col - 16 (m % 2) - 8h (if in 0..7)
+  auto id_frag = [&](int m, uint32_t wbits) {
+    const int i = col - 16 * (m & 1) - 8 * h;
+    uint4 v;
+    v.x = (i == 0 ? wbits : 0u) | (i == 1 ? wbits << 16 : 0u);
+    v.y = (i == 2 ? wbits : 0u) | (i == 3 ? wbits << 16 : 0u);
+    v.z = (i == 4 ? wbits : 0u) | (i == 5 ? wbits << 16 : 0u);
+    v.w = (i == 6 ? wbits : 0u) | (i == 7 ? wbits << 16 : 0u);
+    return v;
+  };
+  // K-step ks of the extended order: the product's NKS, then the identity's
+  auto fetch_q = [&](int ks, uint4 (&dst)[RTW]) {
+#pragma unroll
+    for (int t = 0; t < RTW; ++t) {
+      const int off = ks < NKS ? ks * 512 : (kb + ks - NKS) * 512;
+      uint4 v = *reinterpret_cast<const uint4*>(Qb + qoff[t] + off);
+      v.x ^= qsign;
+      v.y ^= qsign;
+      v.z ^= qsign;
+      v.w ^= qsign;
+      dst[t] = v;
+    }
+  };
+  if constexpr (NID > 0) {
+    // X_k = Q[:, panel]: the identity products alone (c = 1)
+#pragma unroll
+    for (int m = 0; m < NID; ++m) {
+      uint4 aq[RTW];
+      fetch_q(NKS + m, aq);
+      const uint4 bi = id_frag(m, 0x3F80u);
+#pragma unroll
+      for (int t = 0; t < RTW; ++t) P[t][m / 2] = mfma32x32x16(as_bf16x8(aq[t]), as_bf16x8(bi), P[t][m / 2]);
+    }
+  }
 
   for (int s = k - 1; s >= 0; --s) {
     store_x();
@@ -628,36 +659,34 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
     {
       // P += (+-Q) X: Q fragments from L2 two K-steps ahead, X fragments
       // from LDS one K-step ahead
-      constexpr int QPF = 2;
+      constexpr int QPF = 2, NKX = NKS + NID;
       uint4 aq[QPF][RTW], bq[2][CTW];
-      auto fetch_a = [&](int ks, int sl) {
-#pragma unroll
-        for (int t = 0; t < RTW; ++t) {
-          uint4 v = *reinterpret_cast<const uint4*>(Qb + qoff[t] + ks * 512);
-          v.x ^= qsign;
-          v.y ^= qsign;
-          v.z ^= qsign;
-          v.w ^= qsign;
-          aq[sl][t] = v;
-        }
-      };
+      const uint32_t wbits = cnp_coef(s + 1, k) == 2.f ? 0x4000u : 0x3F80u;
       auto fetch_b = [&](int ks, int sl) {
 #pragma unroll
         for (int u = 0; u < CTW; ++u)
           bq[sl][u] = *reinterpret_cast<const uint4*>(Xs + (u * 32 + col) * QP + ks * 16 + 8 * h);
       };
 #pragma unroll
-      for (int i = 0; i < QPF; ++i) fetch_a(i, i);
+      for (int i = 0; i < QPF; ++i) fetch_q(i, aq[i]);
       fetch_b(0, 0);
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int ks = 0; ks < NKX; ++ks) {
         if (ks + 1 < NKS) fetch_b(ks + 1, (ks + 1) & 1);
+        if (ks < NKS) {
 #pragma unroll
-        for (int t = 0; t < RTW; ++t)
+          for (int t = 0; t < RTW; ++t)
 #pragma unroll
-          for (int u = 0; u < CTW; ++u)
-            P[t][u] = mfma32x32x16(as_bf16x8(aq[ks % QPF][t]), as_bf16x8(bq[ks & 1][u]), P[t][u]);
-        if (ks + QPF < NKS) fetch_a(ks + QPF, ks % QPF);
+            for (int u = 0; u < CTW; ++u)
+              P[t][u] = mfma32x32x16(as_bf16x8(aq[ks % QPF][t]), as_bf16x8(bq[ks & 1][u]), P[t][u]);
+        } else {
+          const int m = ks - NKS;
+          const uint4 bi = id_frag(m, wbits);
+#pragma unroll
+          for (int t = 0; t < RTW; ++t)
+            P[t][m / 2] = mfma32x32x16(as_bf16x8(aq[ks % QPF][t]), as_bf16x8(bi), P[t][m / 2]);
+        }
+        if (ks + QPF < NKX) fetch_q(ks + QPF, aq[ks % QPF]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
