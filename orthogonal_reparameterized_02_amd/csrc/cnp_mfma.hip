@@ -469,6 +469,11 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
 // Phase 2 reads the bf16 F_s itself, where the narrower panels keep
 // F_s - w D (a smaller quantity) in bf16; the rounding of that one term is
 // the only difference in arithmetic.
+// Phase 1 stores F_s for phase 2 in the latter's accumulator order: the
+// 32 x 32 tile (rt, ct) is 2 KB, lane L = 32 h + col holding F_s[rt*32 + 8q
+// + 4h + i][ct*32 + col] as its elements 4q + i.  Offset in elements.
+__device__ __forceinline__ long f_tile_off(int rt, int ct) { return (long)(rt * 16 + ct) * 1024; }
+
 __device__ __forceinline__ void wide_tile(int id, int nwg, int npan, int& blk, int& pan) {
   // workgroups are dealt round-robin over the 8 XCDs: give each XCD a
   // contiguous range of (block, panel) pairs, so a block's panels share an
@@ -555,13 +560,16 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
 #pragma unroll
           for (int r = 0; r < 16; ++r) P[t][u][r] = w * Dr[t][u][r];
         } else if (s < k) {
-          // F_s[row][c], row = rt*32 + 8(r/4) + 4h + r%4
-          const int lo = (4 * hh * B + c) * 2;
+          // F_s is stored in this lane's accumulator order (f_tile_off):
+          // the tile's 16 values are 32 contiguous bytes
+          const int so = (int)f_tile_off(rt, J0 / 32 + u) * 2;
+          const u32x4_t v0 = __builtin_amdgcn_raw_buffer_load_b128(rsF, lane * 32, so, 0);
+          const u32x4_t v1 = __builtin_amdgcn_raw_buffer_load_b128(rsF, lane * 32 + 16, so, 0);
+          const uint32_t wv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const unsigned short v = __builtin_amdgcn_raw_buffer_load_b16(
-                rsF, lo, (rt * 32 + 8 * (r / 4) + r % 4) * B * 2, 0);
-            P[t][u][r] = bf2f((bf16)v);
+          for (int e = 0; e < 8; ++e) {
+            P[t][u][2 * e] = __uint_as_float(wv[e] << 16);
+            P[t][u][2 * e + 1] = __uint_as_float(wv[e] & 0xffff0000u);
           }
         } else {
           // s = k: Y_k = w D
@@ -588,13 +596,27 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
       }
   };
   // phase 1: rows J0 .. J0 + PWW - 1 of F_s from Xs, 16-byte stores
+  // phase 1: rows J0 .. J0 + PWW - 1 of F_s (in Xs) in phase 2's
+  // accumulator order, 16-byte stores: chunk v is half v % 2 of lane
+  // (v / 2) % 64 of tile v / 128 (row tile J0 / 32 + tile / 16, column
+  // tile tile % 16); its eight values come from eight rows of Xs
   auto store_f = [&](int s) {
     bf16* F = out_bf + ((long)s * nblk + blk) * B * B;
-    constexpr int VPR = B / 8;  // 16-byte vectors per row
+    constexpr int NCH = (PWW / 32) * 16 * 128;
 #pragma unroll
-    for (int v = threadIdx.x; v < PWW * VPR; v += 512) {
-      const int r = v / VPR, c8 = (v % VPR) * 8;
-      *reinterpret_cast<uint4*>(F + (long)(J0 + r) * B + c8) = *reinterpret_cast<const uint4*>(Xs + r * QP + c8);
+    for (int v = threadIdx.x; v < NCH; v += 512) {
+      const int half = v & 1, L = (v >> 1) & 63, tile = v >> 7;
+      const int rtl = tile / 16, ct = tile % 16, cl = L % 32, hl = L / 32;
+      const bf16* x = Xs + (rtl * 32 + 4 * hl) * QP + ct * 32 + cl;
+      uint4 w;
+      uint32_t* wp = reinterpret_cast<uint32_t*>(&w);
+#pragma unroll
+      for (int p2 = 0; p2 < 4; ++p2) {
+        // elements 8 half + 2 p2 (+1): q = 2 half + p2 / 2, i = 2 (p2 % 2)
+        const int r0 = 8 * (2 * half + p2 / 2) + 2 * (p2 % 2);
+        wp[p2] = (uint32_t)x[r0 * QP] | ((uint32_t)x[(r0 + 1) * QP] << 16);
+      }
+      *reinterpret_cast<uint4*>(F + f_tile_off(J0 / 32 + rtl, ct) + L * 16 + 8 * half) = w;
     }
   };
 
