@@ -447,25 +447,24 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   }
 }
 
-// Blocks of 512: 128-column panels (four per block), eight waves of 64 rows
-// x 128 columns.  Q (512 KB in bf16) does not fit LDS and is read straight
-// from L2 as the MFMA A operand in fragment order (q_off), so what bounds a
-// Horner step is the L2-to-CU traffic of Q: a panel streams all of Q once
-// per step, and four panels per block instead of sixteen cut that traffic
-// to a quarter: each Q fragment now feeds four MFMAs.  The panel X^T
-// (128 x 512 bf16) is the B operand in LDS.
-// Each step's addend is loaded at the start of the step straight into the
-// accumulators (the MFMAs then add the product to it), so its L2 latency is
-// paid once per step, for all eight tiles of a wave together:
-//   forward  X_s = c Q[:, panel] + Q X_{s+1};  Q[row][J0 + c] = -Q[J0 + c][row]
-//            gives four consecutive rows of a lane as one 8-byte piece of
-//            row J0 + c of Q in fragment order;
+// Blocks of 512: panels of 128 columns (forward, phase 2) or 64 (phase 1),
+// eight waves of 64 rows each.  Q (512 KB in bf16) does not fit LDS and is
+// read straight from L2 as the MFMA A operand in fragment order (q_off), so
+// the L2-to-CU traffic of Q bounds a Horner step: a panel streams all of Q
+// once per step, and a 128-column panel feeds each Q fragment to four
+// MFMAs (a 32-column one to one).  The panel X^T is the B operand in LDS.
+// The steps:
+//   forward  X_s = c Q[:, panel] + Q X_{s+1}.  The addend is itself a
+//            product, Q (c E_panel): after the step's 32 K-steps come 2 CTW
+//            more over K = the panel's own columns, each row tile adding one
+//            MFMA with c times an identity block as the B fragment;
 //   phase 1  X_s = F_s^T = w_{s+1} D^T - Q X_{s+1} (the product with -Q: the
-//            A fragments' sign bits flipped); four consecutive rows of a lane
-//            are one 16-byte piece of row J0 + c of D.  The panel of F_s is
-//            stored (bf16) from its LDS copy, whose rows are rows of F_s;
-//   phase 2  Y_s = F_s + Q Y_{s+1}, Y_k = w_{k+1} D: 32 lanes read 32
-//            consecutive columns of a row.
+//            A fragments' sign bits flipped).  The panel's D^T stays in
+//            registers from the first step on; four consecutive rows of a
+//            lane are one 16-byte piece of row J0 + c of D.  F_s goes out
+//            from its LDS copy, whose rows are rows of F_s;
+//   phase 2  Y_s = F_s + Q Y_{s+1}, Y_k = w_{k+1} D: F_s is loaded into the
+//            accumulators at the start of the step.
 // Phase 2 reads the bf16 F_s itself, where the narrower panels keep
 // F_s - w D (a smaller quantity) in bf16; the rounding of that one term is
 // the only difference in arithmetic.
