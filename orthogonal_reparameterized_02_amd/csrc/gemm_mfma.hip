@@ -747,10 +747,10 @@ __device__ __forceinline__ void wait_vm() {
 // lane holds.  The 16-byte chunk index of a token row is XORed with
 // 2 * (token % 4), so the four rows one read touches fall on distinct banks.
 // Output: an fp32 TM x TN partial, staged through LDS for 16-byte stores.
-// A TM x TN tile of a D x D product: TN = TM / 2 gives twice the
-// workgroups of square tiles for the same token splits (and fp32
-// partials); the two column halves of a tile read the same A slabs, and the
-// renumbering below puts them on one XCD, so that A comes from its L2.
+// A TM x TN tile of a D x D product: TN = TM / 2 or TM / 4 gives two or
+// four times the workgroups of square tiles for the same token splits (and
+// fp32 partials); the column parts of a block read the same A slabs, and
+// the renumbering below puts them on one XCD, so that A comes from its L2.
 // One launch can serve two operand pairs of the same D (dG_R and dG_P):
 // batch entries below nb0 read (A0, B0), the rest (A1, B1).  With one token
 // split and P1 set, the second pair writes its sums to P1 instead of after
@@ -1327,11 +1327,14 @@ hipError_t launch_mfma_blocks(int nblk, int T, int width, int b, const bf16* A, 
   return hipErrorInvalidValue;
 }
 
-// Tile width of the D >= 256 reduction (k_tn4): 256 x 128 tiles, twice the
-// workgroups of 256 x 256 ones, while that keeps the launch within one
-// round of the CUs; then as many token splits as fill the CUs.
+// Tile width of the D >= 256 reduction (k_tn4): the narrowest of 64, 128
+// and 256 columns whose tiles still fit one round of the CUs; then as many
+// token splits as fill the CUs.  Narrower tiles mean fewer splits, so fewer
+// fp32 partials to write and reduce (the tiles of a block share their A
+// rows through L2): 32 blocks of 256 take 256 x 64 tiles in 2 splits.
 int tn4_width(int batch, int D) {
   const long tiles256 = (long)batch * (D / 256) * (D / 256);
+  if (4 * tiles256 <= NUM_CU) return 64;
   return 2 * tiles256 <= NUM_CU ? 128 : 256;
 }
 
@@ -1397,7 +1400,10 @@ hipError_t tn4_launch_w(int batch, int nb0, int D, int T, int S, const bf16* A0,
 hipError_t tn4_launch(int batch, int nb0, int D, int T, int S, const bf16* A0, long lda0,
                       const bf16* B0, long ldb0, const bf16* A1, long lda1, const bf16* B1,
                       long ldb1, float* P, hipStream_t s, float* P1 = nullptr) {
-  if (tn4_width(batch, D) == 128)
+  const int w = tn4_width(batch, D);
+  if (w == 64)
+    return tn4_launch_w<64>(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, P, s, P1);
+  if (w == 128)
     return tn4_launch_w<128>(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, P, s, P1);
   return tn4_launch_w<256>(batch, nb0, D, T, S, A0, lda0, B0, ldb0, A1, lda1, B1, ldb1, P, s, P1);
 }
