@@ -139,7 +139,7 @@ __device__ __forceinline__ void q_to_lds(const bf16* __restrict__ Qb, bf16* Qs, 
   }
 }
 
-template <int B, bool QLDS, int MODE>
+template <int B, int MODE>
 __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) void k_cnp_panel(int k, const float* __restrict__ theta,
                                                   const bf16* __restrict__ Qg,
                                                   const float* __restrict__ D,
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   constexpr int RTW = (RT + NWAVE - 1) / NWAVE;     // row tiles per wave
   extern __shared__ __align__(16) unsigned char smem[];
   bf16* Xs = reinterpret_cast<bf16*>(smem);         // [PW][QP]: X^T
-  bf16* Qs = Xs + PW * QP;                          // [B][QP] (QLDS only)
+  bf16* Qs = Xs + PW * QP;                          // [B][QP]
 
   // Workgroups are dealt round-robin over the 8 XCDs; renumber them so each
   // XCD walks a contiguous range of (block, panel) pairs.  The panels of one
@@ -179,13 +179,11 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   // which keeps conditionally stored arrays out of registers)
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
-  u32x4_t qv[QLDS ? QPER : 1];
-  if constexpr (QLDS) {
+  u32x4_t qv[QPER];
 #pragma unroll
-    for (int u = 0; u < QPER; ++u) {
-      const int q = u * NT + threadIdx.x;
-      qv[u] = *reinterpret_cast<const u32x4_t*>(Qb + (q / (B / 8)) * B + (q % (B / 8)) * 8);
-    }
+  for (int u = 0; u < QPER; ++u) {
+    const int q = u * NT + threadIdx.x;
+    qv[u] = *reinterpret_cast<const u32x4_t*>(Qb + (q / (B / 8)) * B + (q % (B / 8)) * 8);
   }
   constexpr int DPER = MODE == MODE_BWD1 ? PW * B / 4 / NT : 1;  // float4 of the D band
   f32x4_t dv[DPER];
@@ -196,8 +194,8 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
   }
 
   // fixed part of the per-step addend, in accumulator layout:
-  //   forward  Q[row][J0+c]   (from the bf16 Q in LDS when it is there: the
-  //                            products use that same rounded Q)
+  //   forward  Q[row][J0+c]   (from the bf16 Q in LDS: the products use that
+  //                            same rounded Q)
   //   phase 1  D^T[row][c] = D[J0+c][row]  (the D band, transposed through LDS)
   //   phase 2  D[row][J0+c]                (row-contiguous global loads)
   float base[RTW][16];
@@ -233,32 +231,12 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     POETX_BAND_PASS(1);
 #undef POETX_BAND_PASS
   }
-  if constexpr (QLDS) {
 #pragma unroll
-    for (int u = 0; u < QPER; ++u) {
-      const int q = u * NT + threadIdx.x;
-      *reinterpret_cast<u32x4_t*>(Qs + (q / (B / 8)) * QP + (q % (B / 8)) * 8) = qv[u];
-    }
-    if constexpr (MODE == MODE_FWD) __syncthreads();  // Q visible for the base
+  for (int u = 0; u < QPER; ++u) {
+    const int q = u * NT + threadIdx.x;
+    *reinterpret_cast<u32x4_t*>(Qs + (q / (B / 8)) * QP + (q % (B / 8)) * 8) = qv[u];
   }
-  if constexpr (MODE == MODE_FWD && !QLDS) {
-    // Q[row][J0+col] = -Q[J0+col][row]: rows J0.. of Q are one row tile in
-    // fragment order, and a lane's four accumulator rows 8a + 4h .. +3 of
-    // row tile rt are four consecutive elements of one 16-byte piece
-#pragma unroll
-    for (int t = 0; t < RTW; ++t) {
-      const int rt = min(wave + t * NWAVE, RT - 1);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const uint2 v = *reinterpret_cast<const uint2*>(
-            Qb + q_off(J0 + col, rt * 32 + 8 * a + 4 * (lane / 32), B, true));
-        base[t][4 * a + 0] = -bf2f((bf16)(v.x & 0xffff));
-        base[t][4 * a + 1] = -bf2f((bf16)(v.x >> 16));
-        base[t][4 * a + 2] = -bf2f((bf16)(v.y & 0xffff));
-        base[t][4 * a + 3] = -bf2f((bf16)(v.y >> 16));
-      }
-    }
-  }
+  if constexpr (MODE == MODE_FWD) __syncthreads();  // Q visible for the base
   f32x16_t X[RTW];
 #pragma unroll
   for (int t = 0; t < RTW; ++t) {
@@ -268,7 +246,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
       if (rt < RT) {
         const int row = rt * 32 + acc_row(r, lane);
         if constexpr (MODE == MODE_FWD) {
-          if constexpr (QLDS) base[t][r] = bf2f(Qs[row * QP + J0 + col]);
+          base[t][r] = bf2f(Qs[row * QP + J0 + col]);
         } else if constexpr (MODE == MODE_BWD2) {
           base[t][r] = Db[(long)row * B + J0 + col];
         }
@@ -310,49 +288,7 @@ __global__ __launch_bounds__(NT, 1) __attribute__((amdgpu_waves_per_eu(1, 2))) v
     f32x16_t P[RTW];
 #pragma unroll
     for (int t = 0; t < RTW; ++t) P[t] = (f32x16_t){};
-    if (!QLDS && wave < RT) {
-      // Q streamed from L2 in fragment order: each fragment load is 1 KB of
-      // whole lines, issued QPF K-steps ahead of its MFMAs (deeper rings
-      // measured no faster: the loop is bound by the CU's L2 bandwidth, 512
-      // KB of Q per step for eight waves); the X fragments come from LDS one
-      // K-step ahead.  Fully unrolled, so every ring index is a constant.
-      constexpr int QPF = 2;
-      constexpr int NKS = B / 16;
-      uint4 bq[2], aq[QPF][RTW];
-      // one element offset per row tile (its K-step 0 fragment; K-step ks
-      // lies ks KB further).  Q is the same in every step, so the offsets
-      // pass through an empty asm each step: otherwise the compiler hoists
-      // all of the wave's Q loads out of the step loop and tries to keep its
-      // 64 KB of Q in registers.  (An offset, not the pointer: a pointer
-      // through asm loses its global address space and the loads become
-      // flat ones, which also count against lgkmcnt.)
-      int qoff[RTW];
-#pragma unroll
-      for (int t = 0; t < RTW; ++t) {
-        qoff[t] = (int)q_off(min(wave + t * NWAVE, RT - 1) * 32 + (lane % 32), 8 * (lane / 32), B, true);
-        asm volatile("" : "+v"(qoff[t]));
-      }
-      const bf16* xrow = Xs + col * QP + 8 * (lane / 32);
-      auto fetch_a = [&](int ks, int s) {  // fragment order: K-step ks is 1 KB further
-#pragma unroll
-        for (int t = 0; t < RTW; ++t)
-          aq[s][t] = *reinterpret_cast<const uint4*>(Qb + qoff[t] + ks * 512);
-      };
-      auto fetch_b = [&](int ks, int s) { bq[s] = *reinterpret_cast<const uint4*>(xrow + ks * 16); };
-#pragma unroll
-      for (int i = 0; i < QPF; ++i) fetch_a(i, i);
-      fetch_b(0, 0);
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        if (ks + 1 < NKS) fetch_b(ks + 1, (ks + 1) & 1);
-#pragma unroll
-        for (int t = 0; t < RTW; ++t)
-          if (RTW * NWAVE == RT || wave + t * NWAVE < RT)
-            P[t] = mfma32x32x16(as_bf16x8(aq[ks % QPF][t]), as_bf16x8(bq[ks & 1]), P[t]);
-        if (ks + QPF < NKS) fetch_a(ks + QPF, ks % QPF);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    } else if (QLDS && wave < RT) {  // waves beyond the block's row tiles only join the barriers
+    if (wave < RT) {  // waves beyond the block's row tiles only join the barriers
       // Q in LDS: operand fragments double-buffered, the reads for k0+16
       // issued before the MFMAs of k0
       uint4 bq[2], aq[2][RTW];
@@ -827,10 +763,9 @@ __global__ __launch_bounds__(256) void k_pack_skew(int b, const float* __restric
 template <int B, int MODE>
 hipError_t launch_panel(int nblk, int k, const float* theta, const bf16* Qg, const float* D,
                         bf16* out_bf, bf16* out_bfT, float* out_f, hipStream_t s) {
-  constexpr bool QLDS = B <= 256;
-  constexpr size_t lds = (size_t)(PW + (QLDS ? B : 0)) * (B + PAD) * sizeof(bf16);
+  constexpr size_t lds = (size_t)(PW + B) * (B + PAD) * sizeof(bf16);
   static_assert(lds <= 160 * 1024, "LDS budget");
-  auto kern = k_cnp_panel<B, QLDS, MODE>;
+  auto kern = k_cnp_panel<B, MODE>;
   // the LDS opt-in is a host call; make it once per kernel, not per launch
   static const hipError_t attr =
       lds > 64 * 1024 ? hipFuncSetAttribute((const void*)kern,
