@@ -697,11 +697,12 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
   }
 }
 
-// Workgroups 0 .. 4 nmain - 1 take blocks 0 .. nmain - 1 in 32 * CTM-column
-// panels; the rest take the remaining blocks in 32 * CTT-column panels.  A
-// block count that leaves a partial last round of 128-column panels (74
-// blocks: 296 panels on 256 CUs) would otherwise run two full panel times;
-// the narrower tail panels fill that round in a fraction of one.
+// Workgroups 0 .. (16 / CTM) nmain - 1 take blocks 0 .. nmain - 1 in
+// 32 * CTM-column panels; the rest take the remaining blocks in
+// 32 * CTT-column panels.  A block count that leaves a partial last round
+// of wide panels (74 blocks: 296 panels of 128 columns on 256 CUs) would
+// otherwise run two full panel times; the narrower tail panels fill that
+// round in a fraction of one.
 template <int MODE, int CTM, int CTT>
 __global__ __launch_bounds__(512, 1) void k_cnp_wide(int k, int nmain, int nblk,
                                                      const bf16* __restrict__ Qg,
@@ -789,18 +790,18 @@ int cu_count() {
   return cached[dev];
 }
 
-// Blocks given 128-column panels (the rest get 64-column ones): the split
-// with the fewest panel times, counting a 64-column panel as 0.55 of a
-// 128-column one (it streams all of Q per step for half the columns) and
-// one panel per CU at a time.
-int wide_split(int nblk, int ncu) {
+// Blocks given the wider panels (pm per block; the rest get pt narrower
+// ones): the split with the fewest panel times, counting a narrower panel
+// as tcost of a wider one (it streams all of Q per step for fewer columns)
+// and one panel per CU at a time.
+int wide_split(int nblk, int ncu, int pm, int pt, double tcost) {
   auto rounds = [&](long wg) { return (double)((wg + ncu - 1) / ncu); };
   int best = nblk;
-  double tbest = rounds(4L * nblk);
-  for (int r = 0; (long)r * ncu <= 4L * nblk; ++r) {
-    const int M = (int)((long)r * ncu / 4);
+  double tbest = rounds((long)pm * nblk);
+  for (int r = 0; (long)r * ncu <= (long)pm * nblk; ++r) {
+    const int M = (int)((long)r * ncu / pm);
     if (M > nblk) break;
-    const double t = rounds(4L * M) + 0.55 * rounds(8L * (nblk - M));
+    const double t = rounds((long)pm * M) + tcost * rounds((long)pt * (nblk - M));
     if (t < tbest - 1e-9) {
       tbest = t;
       best = M;
@@ -812,16 +813,18 @@ int wide_split(int nblk, int ncu) {
 template <int MODE>
 hipError_t launch_wide(int nblk, int k, const bf16* Qg, const float* D, bf16* out_bf,
                        bf16* out_bfT, float* out_f, hipStream_t s) {
-  // the forward and phase 2 take 128-column panels where they fill whole
-  // rounds of the CUs; phase 1 takes 64-column panels throughout
-  constexpr int CTM = MODE == MODE_BWD1 ? 2 : 4, CTT = 2;
+  // the forward and phase 2: 128-column panels where they fill whole rounds
+  // of the CUs, 64-column ones for the rest; phase 1 (which keeps D^T in
+  // registers): 64 and 32
+  constexpr int CTM = MODE == MODE_BWD1 ? 2 : 4, CTT = CTM / 2;
+  constexpr double TCOST = MODE == MODE_BWD1 ? 0.6 : 0.55;
   constexpr size_t lds = (size_t)32 * CTM * (512 + PAD) * sizeof(bf16);
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = k_cnp_wide<MODE, CTM, CTT>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  const int nmain = CTM == CTT ? 0 : wide_split(nblk, cu_count());
+  const int nmain = wide_split(nblk, cu_count(), 16 / CTM, 16 / CTT, TCOST);
   const long nwg = (long)(16 / CTM) * nmain + (long)(16 / CTT) * (nblk - nmain);
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(512), lds, s, k, nmain, nblk, Qg, D, out_bf,
                      out_bfT, out_f);
