@@ -24,6 +24,8 @@
 // MFMA: v_mfma_f32_32x32x16_bf16.  Operand layout (lane l of 64):
 //   A 32x16: A[l%32][8*(l/32) + i], i < 8      B 16x32: B[8*(l/32) + i][l%32]
 //   D 32x32: acc[r] = D[8*(r/4) + 4*(l/32) + r%4][l%32]
+#include <atomic>
+
 #include "kernels.h"
 
 namespace poetx {
@@ -440,13 +442,10 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
   const bf16* Qb = Qg + boff;
   f32x16_t P[RTW][CTW];
   float Dr[DRES ? RTW : 1][DRES ? CTW : 1][DRES ? 16 : 1];
-  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   // The addends are read through buffer resources over one block: a lane's
   // offset is one 32-bit register per column tile, the rest a wave-uniform
   // constant, so no 64-bit address per element stays live.
-  const __amdgpu_buffer_rsrc_t rsQ =
-      __builtin_amdgcn_make_buffer_rsrc((void*)Qb, (short)0, B * B * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(D ? D + boff : nullptr), (short)0, D ? B * B * 4 : 0, 0x00020000);
 
@@ -778,16 +777,17 @@ hipError_t launch_panel(int nblk, int k, const float* theta, const bf16* Qg, con
   return hipGetLastError();
 }
 
+// CUs of the current device, asked once per device (256 on MI355X)
 int cu_count() {
-  static int cached[64] = {};
+  static std::atomic<int> cached[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (!cached[dev]) {
-    int v = 0;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v < 1) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
-    cached[dev] = v;
+    cached[dev].store(v, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return v;
 }
 
 // Blocks given the wider panels (pm per block; the rest get pt narrower
