@@ -239,14 +239,17 @@ def main() -> int:
                              "fwd_bwd": nblocks / ((stages["cnp_fwd"] + stages["cnp_bwd"]) * 1e-6)},
         "stages_us": {k: round(v, 2) for k, v in stages.items()},
         "inner_loop_merge_us": merge_us,
-        "roofline": {"kernel": (f"k_nt4<{1 if b == 256 else 2}>, both launches of the step: "
+        "roofline": {"kernel": (f"k_nt4<{1 if b == 256 else 2}>"
+                                + (" on the int8 weight (dequantized in the kernel)" if args.xq else "")
+                                + ", both launches of the step: "
                                 "Z = V W0f^T with S = Z G_R^T and dV = dZ W0f with dU = dV G_P "
                                 "in the epilogue" if fused else
                                 f"{unfused_dense_kernel(T, m)}, both launches of the step: "
                                 "Z = V W0f^T and dV = dZ W0f"),
                      "bound": "mfma", "achieved": dense_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": dense_tflops / peak,
-                     "traffic": measured_traffic(cfg.name) if fused else None,
+                     # the committed counters are the bf16 kernel's: none for the int8 one
+                     "traffic": measured_traffic(cfg.name) if fused and not args.xq else None,
                      "flops_per_launch": dense_flops, "avg_launch_us": dense_us},
         "wall_s_timed": wall,
         "launch": "eager" if args.eager else "hip_graph",
