@@ -128,6 +128,28 @@ def test_cnp_bwd_finite_differences(rng, b, k):
     np.testing.assert_allclose(g, fd, rtol=0, atol=1e-8 * max(1.0, np.abs(fd).max()))
 
 
+def test_cnp_bwd_batched_finite_differences(rng):
+    """The batched backward differentiates sum_i <dG_i, G(theta_i)> block by
+    block: central differences over coordinates of every block (a swapped
+    block pairing or a wrong block size fails)."""
+    b, k, nblk = 5, 3, 3
+    theta = np.stack([rand_theta(rng, b, 0.2) for _ in range(nblk)])
+    dG = rng.standard_normal((nblk, b, b))
+    g = O.cnp_bwd(theta, dG, b, k)
+    assert g.shape == theta.shape
+
+    def loss(th):
+        return float(np.sum(dG * O.cnp_fwd(th, b, k)))
+
+    h = 1e-6
+    for i in range(nblk):
+        for t in (0, 3, theta.shape[1] - 1):
+            e = np.zeros_like(theta)
+            e[i, t] = h
+            fd = (loss(theta + e) - loss(theta - e)) / (2 * h)
+            assert abs(g[i, t] - fd) <= 1e-8 * max(1.0, abs(fd))
+
+
 def test_cnp_bwd_special_cases(rng):
     b = 7
     dG = rng.standard_normal((b, b))
