@@ -68,6 +68,8 @@ CNP_CASES = [  # nblk, b, k, dtype, sigma
     (37, 512, 5, "bf16", 0.005),
     (74, 512, 5, "bf16", 0.005),   # 128-column panels for 64 blocks, 64-column ones for 10
     (65, 512, 3, "bf16", 0.005),   # the same split with a single 64-column block
+    (64, 512, 4, "bf16", 0.005),   # exactly one round of wide panels, no tail
+    (1, 512, 2, "bf16", 0.005),    # one block: narrow panels only
     (2, 512, 0, "bf16", 0.005),
     (2, 512, 1, "bf16", 0.005),
 ]
