@@ -51,6 +51,10 @@ def main() -> int:
     ap.add_argument("--keep-w0ft", action="store_true",
                     help="also keep the folded weight transposed and let the backward's dense "
                          "product read that copy instead of W0f itself (same results)")
+    ap.add_argument("--fused-gather", action="store_true",
+                    help="run each input-side gather and the block products after it as one "
+                         "pass (bf16, b = 256, gathered width up to 4096) instead of a gather "
+                         "pass and a block pass")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel of each timed step from the host instead of "
                          "replaying one captured HIP graph of the step")
@@ -83,6 +87,7 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
         return torch.from_numpy(a).cuda()
 
+    P.poetx_set_fused_gather(args.fused_gather)  # before the workspaces are sized
     L = POETXLayer(cfg.m, cfg.n, cfg.b, cfg.k, cfg.T, act, xmem=args.xmem, xq=args.xq,
                    keep_w0ft=args.keep_w0ft)
     if args.xq:
@@ -162,6 +167,8 @@ def main() -> int:
     def mean_ms(evs, i, j):
         return float(np.mean([e[i].elapsed_time(e[j]) for e in evs]))
 
+    # (with --fused-gather, gather_x and gather_dy hold the one-pass kernel and
+    # blocks_P, blocks_R_bwd only the event gap)
     fwd_names = ["gather_x", "blocks_P", "dense_Z", "blocks_R", "scatter_y"]
     bwd_names = ["gather_dy", "blocks_R_bwd", "dG_R", "dense_dV", "blocks_P_bwd", "dG_P", "scatter_dx"]
     stages = {nm: mean_ms(fwd_ev, i, i + 1) * 1e3 for i, nm in enumerate(fwd_names)}
@@ -231,7 +238,9 @@ def main() -> int:
                                f"T={T} tokens, {cfg.dtype} activations/W0, fp32 theta"
                                + (", xmem (Z recomputed in the backward)" if args.xmem else "")
                                + (", xq (int8 base weight)" if args.xq else "")
-                               + (", W0f kept transposed too" if args.keep_w0ft else ""),
+                               + (", W0f kept transposed too" if args.keep_w0ft else "")
+                               + (", one-pass gather + block products" if args.fused_gather
+                                  else ""),
                    "m": m, "n": n, "b": b, "k": cfg.k, "tokens": T, "seed": args.seed},
         "mfma_peak_frac": flops / (ms * 1e-3) / (peak * 1e12),
         "step_tflops": flops / (ms * 1e-3) / 1e12,

@@ -350,6 +350,25 @@ int32_t poetx_merge(const poetx_shape* sh, const void* W0f, const void* G_R,
  */
 int32_t poetx_set_stage_events(void* const* events, int32_t count);
 
+/*
+ * poetx_set_fused_gather -- how the layer calls of this process run an
+ * input-side gather and the block products that follow it ("POET-X ...",
+ * technical summary 2.2: the index map reorders data as it is read; 2.3:
+ * batched block products): the forward's U = x[:, pi_P], V = U G_P^T, the
+ * backward's dS = dy[:, pi_R], dZ = dS G_R, and the memory-saving
+ * backward's recompute of V.  on != 0: one pass that gathers straight into
+ * the block products' operands, where the layer is bf16 with b = 256 and
+ * the gathered width (n, or m for dy) is a multiple of 512 up to 4096;
+ * 0 (the default): a gather pass, then a block pass.  Both forms are exact
+ * on the gather and agree with each other to rounding (their block
+ * products sum in different orders); on MI355X the one-pass form is the
+ * slower of the two at the square 4096 workload.  Workspace sizes depend on
+ * the setting: set it before sizing workspaces, and keep it between a
+ * forward call and the backward call that uses its saved buffer.  Returns
+ * the previous setting (0 or 1).
+ */
+int32_t poetx_set_fused_gather(int32_t on);
+
 /* Scratch bytes for poetx_layer_fwd (which = 0), poetx_layer_bwd (1),
  * poetx_layer_fwd_xmem (2), poetx_layer_bwd_xmem (3) or poetx_merge (4);
  * 0 on bad arguments. */

@@ -42,6 +42,7 @@ SIGNATURES = {
     "poetx_fold_scale": (_i, [_i, _p, _p, _p, _p]),
     "poetx_dequant": (_i, [_i, _i, _p, _p, _i, _p, _p]),
     "poetx_set_stage_events": (_i, [_p, _i]),
+    "poetx_set_fused_gather": (_i, [_i]),
 }
 
 

@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 
 #include "../../include/poetx.h"
@@ -108,8 +109,19 @@ inline bool use_mfma(const poetx_shape* sh) { return sh->act == POETX_BF16 && sh
 // workspace layout of the layer calls
 // (xmem: the forward's Z, or the backward's recomputed Z, lives in the
 // workspace instead of the saved buffer)
-struct FwdWs { size_t V, S, Z, total; };
-struct BwdWs { size_t dS, dZ, dV, dU, part, Z, total; };
+struct FwdWs { size_t V, S, Z, Gf, total; };
+struct BwdWs { size_t dS, dZ, dV, dU, part, Z, Gf, total; };
+
+// poetx_set_fused_gather: the gather and its block products as one pass
+std::atomic<int> g_fused_gather{0};
+
+// a side of width W gathers and forms its block products in one pass
+// (gather_blocks.hip: bf16, b = 256, W a multiple of 512 up to 4096) when
+// that form is selected
+inline bool fused_gather(const poetx_shape* sh, int W) {
+  return g_fused_gather.load(std::memory_order_relaxed) && use_mfma(sh) &&
+         gather_blocks_ok(W, sh->b);
+}
 
 FwdWs fwd_ws(const poetx_shape* sh, bool xmem = false) {
   const size_t es = es_of(sh->act), T = sh->T;
@@ -117,7 +129,8 @@ FwdWs fwd_ws(const poetx_shape* sh, bool xmem = false) {
   w.V = 0;
   w.S = w.V + align_up(T * sh->n * es);
   w.Z = w.S + align_up(T * sh->m * es);
-  w.total = w.Z + (xmem ? align_up(T * sh->m * es) : 0);
+  w.Gf = w.Z + (xmem ? align_up(T * sh->m * es) : 0);
+  w.total = w.Gf + (fused_gather(sh, sh->n) ? align_up(gather_blocks_ws_bytes(sh->n, sh->b)) : 0);
   return w;
 }
 
@@ -138,7 +151,12 @@ BwdWs bwd_ws(const poetx_shape* sh, bool xmem = false) {
     part = align_up(std::max(pb, std::max(pr, pp)));
   }
   w.Z = w.part + part;
-  w.total = w.Z + (xmem ? align_up((size_t)sh->T * sh->m * es) : 0);
+  w.Gf = w.Z + (xmem ? align_up((size_t)sh->T * sh->m * es) : 0);
+  // G in fragment order: the R side's for dy, and in the memory-saving mode
+  // the P side's for the recompute of V (one after the other)
+  size_t gf = fused_gather(sh, sh->m) ? gather_blocks_ws_bytes(sh->m, sh->b) : 0;
+  if (xmem && fused_gather(sh, sh->n)) gf = std::max(gf, gather_blocks_ws_bytes(sh->n, sh->b));
+  w.total = w.Gf + align_up(gf);
   return w;
 }
 
@@ -249,11 +267,24 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
   const long bb = (long)b * b;
   hipError_t e;
   mark(0, s);
-  // U = x[:, pi_P]
-  if ((e = launch_permute_cols(T, n, es, x, perm_P, U, s)) != hipSuccess) return dev_fail(e, "gather x");
+  bool gathered = false;
+  if constexpr (sizeof(TS) == 2) {
+    if (fused_gather(sh, n)) {
+      // U = x[:, pi_P] and V_j = U_j G_Pj^T in one pass
+      if ((e = launch_gather_blocks(T, n, x, perm_P, U, G_P, at<TS>(ws, w.Gf), V, nullptr, s)) !=
+          hipSuccess)
+        return dev_fail(e, "gather x + P-side blocks");
+      gathered = true;
+    }
+  }
+  if (!gathered) {
+    // U = x[:, pi_P]
+    if ((e = launch_permute_cols(T, n, es, x, perm_P, U, s)) != hipSuccess)
+      return dev_fail(e, "gather x");
+  }
   mark(1, s);
   // V_j = U_j G_Pj^T
-  if ((e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
+  if (!gathered && (e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
     return dev_fail(e, "P-side blocks");
   mark(2, s);
   {
@@ -299,7 +330,17 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
     // Z = V W0f^T with the kernels the forward used, so Z is bitwise the same
     TS* V = dU;
     TS* Zr = at<TS>(ws, w.Z);
-    if ((e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
+    bool done = false;
+    if constexpr (sizeof(TS) == 2) {
+      if (fused_gather(sh, n)) {
+        // the forward's kernel with the identity map: bitwise its V
+        if ((e = launch_gather_blocks(T, n, U, nullptr, nullptr, G_P, at<TS>(ws, w.Gf), V,
+                                      nullptr, s)) != hipSuccess)
+          return dev_fail(e, "recompute V");
+        done = true;
+      }
+    }
+    if (!done && (e = blocks<TS>(mf, n / b, T, n, b, U, G_P, V, s)) != hipSuccess)
       return dev_fail(e, "recompute V");
     bool fused = false;
     if ((e = dense_fwd<TS>(mf, sh, V, W, Zr, nullptr, nullptr, fused, s)) != hipSuccess)
@@ -309,13 +350,23 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
     Z = at<TS>(saved, saved_Z(sh));
   }
   mark(0, s);
-  // dS = dy[:, pi_R]
-  if ((e = launch_permute_cols(T, m, es, dy, perm_R, dS, s)) != hipSuccess) return dev_fail(e, "gather dy");
+  // dS = dy[:, pi_R], then dZ_i = dS_i G_Ri (B operand G_Ri^T).  An int8
+  // weight W0f = diag(s_f) q_f gives dV = dZ W0f = (dZ diag(s_f)) q_f: the
+  // scale goes on dZ's columns here, where it is one multiply per element
+  // before rounding.
+  bool gathered = false;
+  if constexpr (sizeof(TS) == 2) {
+    if (fused_gather(sh, m)) {
+      if ((e = launch_gather_blocks(T, m, dy, perm_R, dS, GT_R, at<TS>(ws, w.Gf), dZ, W.s, s)) !=
+          hipSuccess)
+        return dev_fail(e, "gather dy + R-side blocks (bwd)");
+      gathered = true;
+    }
+  }
+  if (!gathered && (e = launch_permute_cols(T, m, es, dy, perm_R, dS, s)) != hipSuccess)
+    return dev_fail(e, "gather dy");
   mark(1, s);
-  // dZ_i = dS_i G_Ri  (B operand G_Ri^T).  An int8 weight W0f = diag(s_f) q_f
-  // gives dV = dZ W0f = (dZ diag(s_f)) q_f: the scale goes on dZ's columns
-  // here, where it is one multiply per element before rounding.
-  if ((e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s, W.s)) != hipSuccess)
+  if (!gathered && (e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s, W.s)) != hipSuccess)
     return dev_fail(e, "R-side blocks (bwd)");
   mark(2, s);
   // dG_Ri = dS_i^T Z_i.  On the MFMA path dG_R waits for dG_P and the two
@@ -821,6 +872,10 @@ int32_t poetx_merge(const poetx_shape* sh, const void* W0f, const void* G_R, con
 }
 
 }  // extern "C"
+
+extern "C" int32_t poetx_set_fused_gather(int32_t on) {
+  return g_fused_gather.exchange(on != 0 ? 1 : 0);
+}
 
 extern "C" int32_t poetx_set_stage_events(void* const* events, int32_t count) {
   if (!events) {

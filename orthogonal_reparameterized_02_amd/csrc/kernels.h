@@ -116,6 +116,18 @@ hipError_t launch_mfma_tn2(int nb0, int nb1, int D, int T, const bf16* A0, long 
                            const bf16* B1, long ldb1, float* out1, float* partials,
                            hipStream_t s);
 
+// ---- gather-fused block products (gather_blocks.hip), bf16, b = 256 ------
+// Ug[t][c] = A[t][perm[c]] (perm null: the identity; Ug null: not stored)
+// and Out[t][256 j + n] = sum_k Ug[t][256 j + k] G[j][n][k], column c of Out
+// scaled by cscale[c] before rounding when cscale is set; A, Ug, Out [T][W].
+// Gf: gather_blocks_ws_bytes(W, b) bytes of scratch (G in operand-fragment
+// order).  W a multiple of 512 up to 4096 (gather_blocks_ok).
+bool gather_blocks_ok(int W, int b);
+size_t gather_blocks_ws_bytes(int W, int b);
+hipError_t launch_gather_blocks(int T, int W, const bf16* A, const int32_t* perm, bf16* Ug,
+                                const bf16* G, bf16* Gf, bf16* Out, const float* cscale,
+                                hipStream_t s);
+
 // ---- MFMA Cayley-Neumann panels (cnp_mfma.hip), bf16, b in {64..512} -------
 // ws_Q: nblk*b*b bf16 scratch holding the unpacked skew blocks.
 hipError_t launch_cnp_panel_fwd(int nblk, int b, int k, const float* theta, bf16* G,

@@ -60,6 +60,12 @@ def shape(m: int, n: int, b: int, k: int, T: int, act: int) -> Shape:
     return Shape(m, n, b, k, T, act)
 
 
+def poetx_set_fused_gather(on: bool) -> bool:
+    """Select the one-pass gather + block products for later layer calls
+    (set it before sizing workspaces); returns the previous setting."""
+    return bool(lib().poetx_set_fused_gather(1 if on else 0))
+
+
 def poetx_cnp_workspace_bytes(nblk: int, b: int, k: int, which: int, act: int) -> int:
     return lib().poetx_cnp_workspace_bytes(nblk, b, k, which, act)
 

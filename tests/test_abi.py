@@ -144,6 +144,33 @@ def test_xmem_argument_errors_and_sizes():
                                   FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 3
 
 
+def test_fused_gather_switch_sizes_the_workspace():
+    """poetx_set_fused_gather returns the previous setting; the one-pass
+    form needs room for G in fragment order (W b bf16 per side) where it
+    applies (bf16, b = 256, gathered width a multiple of 512 up to 4096)."""
+    L = _lib.lib()
+    square = _lib.Shape(4096, 4096, 256, 4, 8192, 1)
+    mid = _lib.Shape(2048, 2048, 128, 4, 4096, 1)
+    up = _lib.Shape(14336, 4096, 256, 4, 16384, 1)
+    prev = L.poetx_set_fused_gather(0)
+    try:
+        sizes = {}
+        for on in (0, 1):
+            assert L.poetx_set_fused_gather(on) == 0   # was off (set above, then on = 0)
+            sizes[on] = {nm: [L.poetx_workspace_bytes(C.byref(sh), w) for w in range(4)]
+                         for nm, sh in (("square", square), ("mid", mid), ("up", up))}
+        assert L.poetx_set_fused_gather(0) == 1
+        g = 4096 * 256 * 2
+        assert [b - a for a, b in zip(sizes[0]["square"], sizes[1]["square"])] == [g] * 4
+        assert sizes[0]["mid"] == sizes[1]["mid"]          # b = 128: never one pass
+        # mlp_up: the forward side (n = 4096) only; m = 14336 is too wide, so
+        # the backward grows only in the memory-saving mode (recompute of V)
+        d = [b - a for a, b in zip(sizes[0]["up"], sizes[1]["up"])]
+        assert d == [g, 0, g, g]
+    finally:
+        L.poetx_set_fused_gather(prev)
+
+
 def test_binding_rejects_host_tensors():
     import torch
     from orthogonal_reparameterized_02_amd import poetx as P
