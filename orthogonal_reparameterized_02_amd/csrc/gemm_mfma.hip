@@ -1053,17 +1053,25 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
   }
   // A slabs stream through a ring of four register sets: slab st+5 is
   // requested as soon as slab st+1 leaves its set for LDS, so four slabs are
-  // in flight per workgroup while G_j stays resident
+  // in flight per workgroup while G_j stays resident.  Every step issues the
+  // same loads (buffer loads: rows past T read as zeros, steps past the end
+  // reload the last slab), a token tile leaves at a fixed step of the ring's
+  // turn and the column scales sit in registers, so the wait for a slab
+  // counts only the loads issued after it instead of draining the ring.
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   const int nsteps = ntiles * NS;
+  const int wrows = min(ntiles * TOK, T - tile0 * TOK);
+  const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(Aj + (long)tile0 * TOK * width), (short)0, wrows * width * 2, 0x00020000);
   uint4 ra[4][PA];
   auto aload = [&](uint4 (&r)[PA], int step) {  // step = tile * NS + slab
-    const int t0 = (tile0 + step / NS) * TOK, k0 = (step % NS) * BK;
+    const int stc = min(step, nsteps - 1);
+    const int tr = (stc / NS) * TOK, k0 = (stc % NS) * BK;
 #pragma unroll
     for (int p = 0; p < PA; ++p) {
-      const int row = t0 + p * RPP + lr;
-      r[p] = (step < nsteps && row < T)
-                 ? *reinterpret_cast<const uint4*>(Aj + (long)row * width + k0 + lc * 8)
-                 : make_uint4(0, 0, 0, 0);
+      const int row = tr + p * RPP + lr;
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rsA, (row * width + k0 + lc * 8) * 2, 0, 0);
+      r[p] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   };
   auto astore = [&](const uint4 (&r)[PA], int buf) {
@@ -1071,6 +1079,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
 #pragma unroll
     for (int p = 0; p < PA; ++p) *reinterpret_cast<uint4*>(As + lds_off(p * RPP + lr, lc)) = r[p];
   };
+  // the lane's column scales (b = 256; with b = 128 the registers are
+  // short, and the staging below reads them)
+  constexpr bool SCV = B == 256;
+  float scv[FN];
+#pragma unroll
+  for (int jj = 0; jj < FN; ++jj)
+    scv[jj] = SCV && cscale ? cscale[(long)j * B + wn * TN + jj * 32 + lane % 32] : 1.0f;
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -1083,38 +1098,45 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
   astore(ra[0], 0);
   aload(ra[0], 4);
   __syncthreads();
-  for (int q = 0; q < nsteps; q += 4) {
+  constexpr int TPI = 4 / NS;  // token tiles per turn of the ring (four steps)
+  static_assert(NS * TPI == 4, "four steps per turn");
+  for (int tile = 0; tile < ntiles; tile += TPI) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int st = q + u;
-      if (st < nsteps) {
-        mma_slab<CF>(As0 + (u & 1) * A_SLAB, Gs + (st % NS) * B * ROWB, acc, wm, wn, lane);
-        if (st % NS == NS - 1) {  // token tile complete: store, restart the accumulators
-          // the A buffer just consumed stages the tile in passes of PROWS rows
-          // so the global stores cover whole 128-byte row segments
-          const int t0 = (tile0 + st / NS) * TOK;
-          constexpr int PROWS = A_SLAB / (B * 2);
-          char* stg = As0 + (u & 1) * A_SLAB;
-          __syncthreads();
-#pragma unroll
-          for (int p = 0; p < TOK / PROWS; ++p) {
-            acc_to_slabs<FM, FN>(acc, stg, PROWS * ROWB, wm * TM, wn * TN, lane, p * PROWS,
-                                 (p + 1) * PROWS, cscale ? cscale + (long)j * B : nullptr);
-            __syncthreads();
-            slabs_to_global_buf<PROWS, B, NTH>(stg, Oj, width, t0 + p * PROWS, 0, T);
-            __syncthreads();
-          }
+      const int st = tile * NS + u;
+      mma_slab<CF>(As0 + (u & 1) * A_SLAB, Gs + (u % NS) * B * ROWB, acc, wm, wn, lane);
+      // slab st+1 into the other A buffer (free since the last barrier)
+      astore(ra[(u + 1) & 3], (u + 1) & 1);
+      aload(ra[(u + 1) & 3], st + 5);
+      if (u % NS == NS - 1 && (TPI == 1 || tile + u / NS < ntiles)) {
+        // token tile complete: the A buffer just consumed stages it in
+        // passes of PROWS rows so the global stores cover whole 128-byte
+        // row segments; then the accumulators restart
+        const int t0 = (tile0 + tile + u / NS) * TOK;
+        constexpr int PROWS = A_SLAB / (B * 2);
+        char* stg = As0 + (u & 1) * A_SLAB;
+        // column scales on the fp32 sums (1 without cscale: x * 1.0f is x)
+        if constexpr (SCV) {
 #pragma unroll
           for (int i = 0; i < FM; ++i)
 #pragma unroll
-            for (int jj = 0; jj < FN; ++jj) acc[i][jj] = (f32x16_t){};
-        }
-        if (st + 1 < nsteps) {
-          astore(ra[(u + 1) & 3], (u + 1) & 1);
-          aload(ra[(u + 1) & 3], st + 5);
+            for (int jj = 0; jj < FN; ++jj) acc[i][jj] *= scv[jj];
         }
         __syncthreads();
+#pragma unroll
+        for (int p = 0; p < TOK / PROWS; ++p) {
+          acc_to_slabs<FM, FN>(acc, stg, PROWS * ROWB, wm * TM, wn * TN, lane, p * PROWS,
+                               (p + 1) * PROWS, SCV || !cscale ? nullptr : cscale + (long)j * B);
+          __syncthreads();
+          slabs_to_global_buf<PROWS, B, NTH>(stg, Oj, width, t0 + p * PROWS, 0, T);
+          __syncthreads();
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int jj = 0; jj < FN; ++jj) acc[i][jj] = (f32x16_t){};
       }
+      __syncthreads();
     }
   }
 }
@@ -1314,6 +1336,9 @@ hipError_t blocks_launch(int nblk, int T, int width, const bf16* A, const bf16* 
     const long cost = rounds * (p + 2);
     if (best < 0 || cost < best || (cost == best && sp < splits)) best = cost, per = p, splits = sp;
   }
+  // a workgroup's rows of A lie in one buffer range: per TOK width 2 < 2^31
+  while (per > 1 && (long)per * TOK * width * 2 >= (1L << 31)) per = (per + 1) / 2;
+  splits = (tiles + per - 1) / per;
   hipLaunchKernelGGL(kern, dim3(nblk, splits), dim3(64 * WM * WN), lds, s, T, width, per, A, G,
                      Out, cscale);
   return hipGetLastError();
