@@ -561,8 +561,17 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
   int qoff[RTW];
 #pragma unroll
   for (int t = 0; t < RTW; ++t) qoff[t] = (int)q_off((wave * RTW + t) * 32 + col, 8 * h, B, true);
-  // phase 1 multiplies by -Q: flip the sign bits of its bf16 fragments
+  // phase 1 multiplies by -Q: the sign bits of its bf16 fragments flip as
+  // the products take them (flipped at the load, each load would be waited
+  // for at once instead of two K-steps later)
   const uint32_t qsign = (MODE == MODE_BWD1) ? 0x80008000u : 0u;
+  auto qfrag = [&](uint4 v) {
+    v.x ^= qsign;
+    v.y ^= qsign;
+    v.z ^= qsign;
+    v.w ^= qsign;
+    return as_bf16x8(v);
+  };
   // The forward's addend c Q[:, panel] = Q (c E_panel) is a product too:
   // after the step's own K-steps come 2 CTW more over K = the panel's
   // columns, each row tile taking one product with c times an identity
@@ -586,12 +595,7 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
 #pragma unroll
     for (int t = 0; t < RTW; ++t) {
       const int off = ks < NKS ? ks * 512 : (kb + ks - NKS) * 512;
-      uint4 v = *reinterpret_cast<const uint4*>(Qb + qoff[t] + off);
-      v.x ^= qsign;
-      v.y ^= qsign;
-      v.z ^= qsign;
-      v.w ^= qsign;
-      dst[t] = v;
+      dst[t] = *reinterpret_cast<const uint4*>(Qb + qoff[t] + off);
     }
   };
   if constexpr (NID > 0) {
@@ -634,7 +638,7 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
           for (int t = 0; t < RTW; ++t)
 #pragma unroll
             for (int u = 0; u < CTW; ++u)
-              P[t][u] = mfma32x32x16(as_bf16x8(aq[ks % QPF][t]), as_bf16x8(bq[ks & 1][u]), P[t][u]);
+              P[t][u] = mfma32x32x16(qfrag(aq[ks % QPF][t]), as_bf16x8(bq[ks & 1][u]), P[t][u]);
         } else {
           const int m = ks - NKS;
           const uint4 bi = id_frag(m, wbits);
