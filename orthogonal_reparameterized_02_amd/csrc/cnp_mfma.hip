@@ -449,11 +449,14 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
   const __amdgpu_buffer_rsrc_t rsD = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(D ? D + boff : nullptr), (short)0, D ? B * B * 4 : 0, 0x00020000);
 
-  // P = the addend of step s (s = k: the starting X), every tile at once
-  auto load_addend = [&](int s) {
+  // P = the addend of step s (s = k: the starting X), every tile at once.
+  // inloop: s < k is known (the step loop), so the tiles' loads form one
+  // straight run and all go out before the first is waited for.
+  auto load_addend = [&](int s, bool inloop) {
     const float w = (MODE == MODE_FWD) ? (s == k ? 1.f : cnp_coef(s + 1, k)) : cnp_wcoef(s + 1, k);
+    const bool before_k = inloop || s < k;
     if constexpr (DRES) {
-      if (s < k) {
+      if (before_k) {
 #pragma unroll
         for (int t = 0; t < RTW; ++t)
 #pragma unroll
@@ -467,7 +470,7 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
     asm volatile("" : "+v"(c0), "+v"(hh));  // recomputed per step, not kept
     __amdgpu_buffer_rsrc_t rsF = rsD;
     if constexpr (MODE == MODE_BWD2) {
-      if (s < k)
+      if (before_k)
         rsF = __builtin_amdgcn_make_buffer_rsrc((void*)(out_bf + ((long)s * nblk + blk) * B * B),
                                                (short)0, B * B * 2, 0x00020000);
     }
@@ -493,7 +496,7 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) P[t][u][r] = w * Dr[t][u][r];
-        } else if (s < k) {
+        } else if (before_k) {
           // F_s is stored in this lane's accumulator order (f_tile_off):
           // the tile's 16 values are 32 contiguous bytes
           const int so = (int)f_tile_off(rt, J0 / 32 + u) * 2;
@@ -554,7 +557,7 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
     }
   };
 
-  load_addend(k);
+  load_addend(k, false);
   // one offset per row tile (its K-step 0 fragment; K-step ks lies ks KB
   // further), passed through an empty asm each step so that the compiler
   // does not hoist the wave's Q loads out of the step loop
@@ -613,7 +616,7 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
   for (int s = k - 1; s >= 0; --s) {
     store_x();
     __syncthreads();
-    load_addend(s);
+    load_addend(s, true);
 #pragma unroll
     for (int t = 0; t < RTW; ++t) asm volatile("" : "+v"(qoff[t]));
     {
