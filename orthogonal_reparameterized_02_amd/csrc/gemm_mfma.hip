@@ -1036,21 +1036,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
   if (ntiles <= 0) return;
   const bf16* Aj = A + (long)j * B;
   bf16* Oj = Out + (long)j * B;
-  // G_j -> LDS, every load in flight first
-  {
-    const bf16* Gj = G + (long)j * B * B;
-    uint4 gv[NS][PG];
+  // G_j -> registers first (from L2); the first A slabs (from HBM) go out
+  // before G's LDS writes wait for G
+  const bf16* Gj = G + (long)j * B * B;
+  uint4 gv[NS][PG];
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int p = 0; p < PG; ++p)
-        gv[s][p] = *reinterpret_cast<const uint4*>(Gj + (long)(p * RPP + lr) * B + s * BK + lc * 8);
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int p = 0; p < PG; ++p)
-        *reinterpret_cast<uint4*>(Gs + s * B * ROWB + lds_off(p * RPP + lr, lc)) = gv[s][p];
-  }
+    for (int p = 0; p < PG; ++p)
+      gv[s][p] = *reinterpret_cast<const uint4*>(Gj + (long)(p * RPP + lr) * B + s * BK + lc * 8);
   // A slabs stream through a ring of four register sets: slab st+5 is
   // requested as soon as slab st+1 leaves its set for LDS, so four slabs are
   // in flight per workgroup while G_j stays resident.  Every step issues the
@@ -1095,6 +1089,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_blocks(int T, int width, in
   aload(ra[1], 1);
   aload(ra[2], 2);
   aload(ra[3], 3);
+#pragma unroll
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int p = 0; p < PG; ++p)
+      *reinterpret_cast<uint4*>(Gs + s * B * ROWB + lds_off(p * RPP + lr, lc)) = gv[s][p];
   astore(ra[0], 0);
   aload(ra[0], 4);
   __syncthreads();
