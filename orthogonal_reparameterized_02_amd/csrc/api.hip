@@ -380,7 +380,10 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
   mark(3, s);
   {
     // dV = dZ W0f and, where the dense kernel carries the block epilogue
-    // (b = 128, 256), dU_j = dV_j G_Pj in the same kernel.  The weight is
+    // (b = 128, 256), dU_j = dV_j G_Pj in the same kernel.  dU goes out
+    // non-temporally: the dG reduction runs between it and the dx scatter,
+    // and dirty dU lines in the last-level cache would have to be written
+    // back to make room for that pass's reads.  The weight is
     // read as W0fT (N-major) when the caller keeps that copy, else straight
     // from W0f (K-major): the same products in the same order.
     bool fused = false, dv_done = false;
@@ -390,17 +393,19 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
         // dV = dZ' q_f (B operand q_fT)
         fused = epi;
         if ((e = launch_mfma_nt_q(T, n, m, b, dZ, m, W.qT, m, dV, n, nullptr,
-                                  fused ? GT_P : nullptr, fused ? dU : nullptr, n, s)) != hipSuccess)
+                                  fused ? GT_P : nullptr, fused ? dU : nullptr, n, s, 2)) !=
+            hipSuccess)
           return dev_fail(e, "W0 product (bwd)");
         dv_done = true;
       } else if (mf && W.fT && epi) {
-        if ((e = launch_mfma_nt_block(T, n, m, b, dZ, m, W.fT, m, dV, n, GT_P, dU, n, s)) != hipSuccess)
+        if ((e = launch_mfma_nt_block(T, n, m, b, dZ, m, W.fT, m, dV, n, GT_P, dU, n, s, 2)) !=
+            hipSuccess)
           return dev_fail(e, "W0 product + P-side blocks (bwd)");
         fused = dv_done = true;
       } else if (mf && !W.fT && mfma_nt_kmajor_ok(T, n, m, m, n, n)) {
         fused = epi;
         if ((e = launch_mfma_nt_kmajor(T, n, m, b, dZ, m, W.f, n, dV, n, fused ? GT_P : nullptr,
-                                       fused ? dU : nullptr, n, s)) != hipSuccess)
+                                       fused ? dU : nullptr, n, s, 2)) != hipSuccess)
           return dev_fail(e, "W0 product (bwd)");
         dv_done = true;
       }

@@ -244,10 +244,12 @@ __device__ __forceinline__ void acc_to_slabsT(const f32x16_t (&acc)[FM][FN], cha
 // range and are dropped by the hardware, so there is no branch; every column
 // of the tile must exist (callers have N % COLS == 0).  Offsets stay below
 // ROWS * ldc * 2 < 2^31 (host-checked).  The range is clamped at zero rows:
-// a negative count would wrap to an unbounded range.
+// a negative count would wrap to an unbounded range.  nt: non-temporal
+// stores, for outputs that no kernel reads soon (they then hold no space in
+// the last-level cache that the next kernels' reads would have to evict).
 template <int ROWS, int COLS, int NTH>
 __device__ __forceinline__ void slabs_to_global_buf(const char* lds, bf16* __restrict__ C, long ldc,
-                                                    int row0, int col0, int M) {
+                                                    int row0, int col0, int M, bool nt = false) {
   constexpr int CHUNKS = ROWS * COLS / 8;
   static_assert(CHUNKS % NTH == 0 && (ROWS & (ROWS - 1)) == 0, "store split");
   typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
@@ -268,7 +270,8 @@ __device__ __forceinline__ void slabs_to_global_buf(const char* lds, bf16* __res
     for (int u = 0; u < CHUNKS / NTH; ++u) {
       const int s = u / (ROWS / RSTEP), ru = (u % (ROWS / RSTEP)) * RSTEP;
       const u32x4v v = *reinterpret_cast<const u32x4v*>(lds + s * ROWS * ROWB + lds_off(ru + r0, c));
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs, vbase + (ru * (int)ldc + s * 64) * 2, 0, 0);
+      if (nt) __builtin_amdgcn_raw_buffer_store_b128(v, rs, vbase + (ru * (int)ldc + s * 64) * 2, 0, 2);
+      else __builtin_amdgcn_raw_buffer_store_b128(v, rs, vbase + (ru * (int)ldc + s * 64) * 2, 0, 0);
     }
   } else {
 #pragma unroll
@@ -276,7 +279,8 @@ __device__ __forceinline__ void slabs_to_global_buf(const char* lds, bf16* __res
       const int q = u * NTH + threadIdx.x;
       const int s = q / (ROWS * 8), r = (q >> 3) & (ROWS - 1);
       const u32x4v v = *reinterpret_cast<const u32x4v*>(lds + s * ROWS * ROWB + lds_off(r, c));
-      __builtin_amdgcn_raw_buffer_store_b128(v, rs, (r * (int)ldc + s * 64 + c * 8) * 2, 0, 0);
+      if (nt) __builtin_amdgcn_raw_buffer_store_b128(v, rs, (r * (int)ldc + s * 64 + c * 8) * 2, 0, 2);
+      else __builtin_amdgcn_raw_buffer_store_b128(v, rs, (r * (int)ldc + s * 64 + c * 8) * 2, 0, 0);
     }
   }
 }
@@ -417,12 +421,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_nt(
 // 32 j + 16 h + [0, 8) and + [8, 16); the A reads follow the same K order.
 // SC: column c of C is multiplied by cscale[bt * sS + c] (fp32, before
 // rounding), which applies a per-output-row weight scale.
+// ntmask: bit 0 stores C, bit 1 stores E non-temporally.
 template <int EPI, int BMODE, bool SC>
 __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_nt4(
     int M, int N, int K, const bf16* __restrict__ A, long lda, long sA, const void* __restrict__ Bv,
     long ldb, long sB, bf16* __restrict__ Cm, long ldc, long sC, int tilesM, int tilesN,
     const bf16* __restrict__ Bk, bf16* __restrict__ E, long lde, const float* __restrict__ cscale,
-    long sS) {
+    long sS, int ntmask) {
   constexpr int BM = 256, BN = 256, TM = 128, TN = 128, FM = 4, FN = 4, NTH = 256;
   constexpr int OPB = 256 * ROWB;  // one operand's 256 rows of a 64-wide slab: 32 KB
   constexpr bool BQ = BMODE == 1, BNN = BMODE == 2;
@@ -687,7 +692,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
         gb[f][j] = as_bf16x8(*reinterpret_cast<const uint4*>(Gw + j * 32 * EB + f * 16));
   }
   __syncthreads();
-  slabs_to_global_buf<BM, BN, NTH>(smem, Cm, ldc, m0, n0, M);
+  slabs_to_global_buf<BM, BN, NTH>(smem, Cm, ldc, m0, n0, M, (ntmask & 1) != 0);
   if constexpr (EPI != 0) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -721,7 +726,7 @@ __global__ __launch_bounds__(256, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) 
     __syncthreads();  // every wave is done with the C tile
     acc_to_slabsT<FM, FN>(acc, smem, SLAB, wm * TM, wn * TN, lane);
     __syncthreads();
-    slabs_to_global_buf<BM, BN, NTH>(smem, E, lde, m0, n0, M);
+    slabs_to_global_buf<BM, BN, NTH>(smem, E, lde, m0, n0, M, (ntmask & 2) != 0);
   }
 }
 
@@ -1218,7 +1223,7 @@ template <int EPI, int BMODE = 0, bool SC = false>
 hipError_t nt4_launch_t(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                         const void* B, long ldb, long sB, bf16* C, long ldc, long sC,
                         const bf16* Bk, bf16* E, long lde, hipStream_t s, const float* cscale,
-                        long sS) {
+                        long sS, int ntmask) {
   auto kern = k_nt4<EPI, BMODE, SC>;
   constexpr int lds = 5 * 256 * ROWB;
   static_assert(lds <= 160 * 1024, "LDS budget");
@@ -1226,7 +1231,7 @@ hipError_t nt4_launch_t(int batch, int M, int N, int K, const bf16* A, long lda,
   if (attr != hipSuccess) return attr;
   const int tM = (M + 255) / 256, tN = (N + 255) / 256;
   hipLaunchKernelGGL(kern, dim3(tM * tN, batch), dim3(256), lds, s, M, N, K, A, lda, sA, B, ldb,
-                     sB, C, ldc, sC, tM, tN, Bk, E, lde, cscale, sS);
+                     sB, C, ldc, sC, tM, tN, Bk, E, lde, cscale, sS, ntmask);
   return hipGetLastError();
 }
 
@@ -1236,12 +1241,12 @@ template <int EPI, int BMODE = 0>
 hipError_t nt4_launch(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
                       const void* B, long ldb, long sB, bf16* C, long ldc, long sC, const bf16* Bk,
                       bf16* E, long lde, hipStream_t s, const float* cscale = nullptr,
-                      long sS = 0) {
+                      long sS = 0, int ntmask = 0) {
   if (cscale)
     return nt4_launch_t<EPI, BMODE, true>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, Bk, E,
-                                       lde, s, cscale, sS);
+                                       lde, s, cscale, sS, ntmask);
   return nt4_launch_t<EPI, BMODE, false>(batch, M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, Bk, E,
-                                      lde, s, nullptr, 0);
+                                      lde, s, nullptr, 0, ntmask);
 }
 
 hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long lda, long sA,
@@ -1268,12 +1273,17 @@ bool mfma_nt_block_ok(int M, int N, int K, int b) {
 
 hipError_t launch_mfma_nt_block(int M, int N, int K, int b, const bf16* A, long lda,
                                 const bf16* B, long ldb, bf16* C, long ldc, const bf16* Bk,
-                                bf16* E, long lde, hipStream_t s) {
+                                bf16* E, long lde, hipStream_t s, int ntmask) {
   if (!nt4_ld_ok(lda, ldb, ldc) || (E && !nt4_ld_ok(lda, ldb, lde))) return hipErrorInvalidValue;
-  if (!E) return nt4_launch<0>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s);
-  if (b == 128) return nt4_launch<2>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+  if (!E)
+    return nt4_launch<0>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s,
+                         nullptr, 0, ntmask);
+  if (b == 128)
+    return nt4_launch<2>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s, nullptr, 0,
+                         ntmask);
   if (b != 256) return hipErrorInvalidValue;
-  return nt4_launch<1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+  return nt4_launch<1>(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, Bk, E, lde, s, nullptr, 0,
+                       ntmask);
 }
 
 bool mfma_nt_kmajor_ok(int M, int N, int K, long lda, long ldb, long ldc) {
@@ -1283,15 +1293,18 @@ bool mfma_nt_kmajor_ok(int M, int N, int K, long lda, long ldb, long ldc) {
 
 hipError_t launch_mfma_nt_kmajor(int M, int N, int K, int b, const bf16* A, long lda,
                                  const bf16* Bkn, long ldb, bf16* C, long ldc, const bf16* Bk,
-                                 bf16* E, long lde, hipStream_t s) {
+                                 bf16* E, long lde, hipStream_t s, int ntmask) {
   if (!mfma_nt_kmajor_ok(M, N, K, lda, ldb, ldc) || (E && !nt4_ld_ok(lda, ldb, lde)))
     return hipErrorInvalidValue;
   if (!E)
-    return nt4_launch<0, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s);
+    return nt4_launch<0, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s,
+                            nullptr, 0, ntmask);
   if (b == 128)
-    return nt4_launch<2, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+    return nt4_launch<2, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, Bk, E, lde, s, nullptr,
+                            0, ntmask);
   if (b != 256) return hipErrorInvalidValue;
-  return nt4_launch<1, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, Bk, E, lde, s);
+  return nt4_launch<1, 2>(1, M, N, K, A, lda, 0, Bkn, ldb, 0, C, ldc, 0, Bk, E, lde, s, nullptr, 0,
+                          ntmask);
 }
 
 bool mfma_nt_q_ok(int M, int N, int K, long lda, long ldb, long ldc) {
@@ -1300,16 +1313,18 @@ bool mfma_nt_q_ok(int M, int N, int K, long lda, long ldb, long ldc) {
 
 hipError_t launch_mfma_nt_q(int M, int N, int K, int b, const bf16* A, long lda, const int8_t* Bq,
                             long ldb, bf16* C, long ldc, const float* cscale, const bf16* Bk,
-                            bf16* E, long lde, hipStream_t s) {
+                            bf16* E, long lde, hipStream_t s, int ntmask) {
   if (!mfma_nt_q_ok(M, N, K, lda, ldb, ldc) || (E && !nt4_ld_ok(lda, ldb, lde)))
     return hipErrorInvalidValue;
   if (!E)
     return nt4_launch<0, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, nullptr, nullptr, 0, s,
-                               cscale, 0);
+                               cscale, 0, ntmask);
   if (b == 128)
-    return nt4_launch<2, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, Bk, E, lde, s, cscale, 0);
+    return nt4_launch<2, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, Bk, E, lde, s, cscale, 0,
+                            ntmask);
   if (b != 256) return hipErrorInvalidValue;
-  return nt4_launch<1, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, Bk, E, lde, s, cscale, 0);
+  return nt4_launch<1, 1>(1, M, N, K, A, lda, 0, Bq, ldb, 0, C, ldc, 0, Bk, E, lde, s, cscale, 0,
+                          ntmask);
 }
 
 bool mfma_blocks_ok(int b) { return b == 128 || b == 256; }

@@ -72,9 +72,11 @@ hipError_t launch_mfma_nt(int batch, int M, int N, int K, const bf16* A, long ld
 // 128), E[:, g] = C[:, g] Bk[g]^T with Bk [N/b][b][b].
 // E == nullptr: C only, from the same main loop (bitwise the same C).
 bool mfma_nt_block_ok(int M, int N, int K, int b);
+// ntmask: bit 0 stores C, bit 1 stores E non-temporally (outputs no kernel
+// reads soon; they then take no room in the last-level cache).
 hipError_t launch_mfma_nt_block(int M, int N, int K, int b, const bf16* A, long lda,
                                 const bf16* B, long ldb, bf16* C, long ldc, const bf16* Bk,
-                                bf16* E, long lde, hipStream_t s);
+                                bf16* E, long lde, hipStream_t s, int ntmask = 0);
 // C = A B^T with B given K-major, Bkn = B^T [K][N] (row pitch ldb >= N):
 // the dense product of the backward, dV = dZ W0f, read from W0f itself;
 // bitwise the result of launch_mfma_nt_block on the transposed copy, block
@@ -82,7 +84,7 @@ hipError_t launch_mfma_nt_block(int M, int N, int K, int b, const bf16* A, long 
 bool mfma_nt_kmajor_ok(int M, int N, int K, long lda, long ldb, long ldc);
 hipError_t launch_mfma_nt_kmajor(int M, int N, int K, int b, const bf16* A, long lda,
                                  const bf16* Bkn, long ldb, bf16* C, long ldc, const bf16* Bk,
-                                 bf16* E, long lde, hipStream_t s);
+                                 bf16* E, long lde, hipStream_t s, int ntmask = 0);
 // C = (A Bq^T) diag(cscale) for an int8 Bq [N][K] (row pitch ldb bytes): the
 // dense product on a quantized weight, widened to bf16 inside the kernel's
 // operand path (exact) with the per-row weight scale applied to the fp32
@@ -90,7 +92,7 @@ hipError_t launch_mfma_nt_kmajor(int M, int N, int K, int b, const bf16* A, long
 bool mfma_nt_q_ok(int M, int N, int K, long lda, long ldb, long ldc);
 hipError_t launch_mfma_nt_q(int M, int N, int K, int b, const bf16* A, long lda, const int8_t* Bq,
                             long ldb, bf16* C, long ldc, const float* cscale, const bf16* Bk,
-                            bf16* E, long lde, hipStream_t s);
+                            bf16* E, long lde, hipStream_t s, int ntmask = 0);
 // per-token block products for b in {128, 256}:
 // Out[t][j b + n] = sum_k A[t][j b + k] G[j][n][k]  (A, Out row pitch `width`),
 // column c of Out scaled by cscale[c] before rounding when cscale is set
