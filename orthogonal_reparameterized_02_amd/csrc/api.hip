@@ -278,8 +278,8 @@ int32_t layer_fwd_impl(const poetx_shape* sh, const TS* x, const TS* G_P, const 
     }
   }
   if (!gathered) {
-    // U = x[:, pi_P]
-    if ((e = launch_permute_cols(T, n, es, x, perm_P, U, s)) != hipSuccess)
+    // U = x[:, pi_P] (plain stores: the block pass reads U next)
+    if ((e = launch_permute_cols(T, n, es, x, perm_P, U, s, false)) != hipSuccess)
       return dev_fail(e, "gather x");
   }
   mark(1, s);
@@ -363,7 +363,7 @@ int32_t layer_bwd_impl(const poetx_shape* sh, const TS* dy, const TS* GT_P, cons
       gathered = true;
     }
   }
-  if (!gathered && (e = launch_permute_cols(T, m, es, dy, perm_R, dS, s)) != hipSuccess)
+  if (!gathered && (e = launch_permute_cols(T, m, es, dy, perm_R, dS, s, false)) != hipSuccess)
     return dev_fail(e, "gather dy");
   mark(1, s);
   if (!gathered && (e = blocks<TS>(mf, m / b, T, m, b, dS, GT_R, dZ, s, W.s)) != hipSuccess)

@@ -23,13 +23,16 @@ __host__ __device__ inline float cnp_wcoef(int p, int k) {
 hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
                        const int32_t* pP, void* W0f, void* W0fT, int32_t* pRinv,
                        int32_t* pPinv, hipStream_t s);
-// out[r][c] = in[r][idx[c]] for r < rows, c < width; es = element bytes (2|4)
+// out[r][c] = in[r][idx[c]] for r < rows, c < width; es = element bytes (2|4);
+// nt_store: non-temporal stores (for an output that the next kernel does
+// not read; plain stores leave it in the last-level cache for that kernel)
 hipError_t launch_permute_cols(int rows, int width, int es, const void* in,
-                               const int32_t* idx, void* out, hipStream_t s);
+                               const int32_t* idx, void* out, hipStream_t s,
+                               bool nt_store = true);
 // out[r][c] = in[rmap[r]][idx[c]] ([rows][width], es = element bytes 2|4)
 hipError_t launch_permute_rows_cols(int rows, int width, int es, const void* in,
                                     const int32_t* rmap, const int32_t* idx, void* out,
-                                    hipStream_t s);
+                                    hipStream_t s, bool nt_store = true);
 // out[j][i] = in[i][j], in [m][n]
 hipError_t launch_transpose(int m, int n, int es, const void* in, void* out, hipStream_t s);
 // out = bf16(scale * q) for int8 q [rows][cols] (cols % 16 == 0); the scale

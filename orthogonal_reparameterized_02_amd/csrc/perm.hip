@@ -63,7 +63,8 @@ __global__ __launch_bounds__(PERM_THREADS) void k_permute_rows_lds(
 // up to MAXV 16-byte output vectors per row.  Every row load and the
 // thread's indices (16-byte vector loads) go out before the first LDS write;
 // one barrier, then each thread gathers its vectors of every row from LDS.
-template <typename E, int NTHR, int RPW, int MAXV>
+// Rows are read non-temporally; NTS: the stores too.
+template <typename E, int NTHR, int RPW, int MAXV, bool NTS>
 __global__ __launch_bounds__(NTHR) void k_permute_rows_v(int rows, int width,
                                                          const E* __restrict__ in,
                                                          const int32_t* __restrict__ rmap,
@@ -121,7 +122,9 @@ __global__ __launch_bounds__(NTHR) void k_permute_rows_v(int rows, int width,
         }
         u32x4 pk;
         __builtin_memcpy(&pk, t, 16);
-        __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(out + (long)(r0 + rr) * width) + v);
+        u32x4* dst = reinterpret_cast<u32x4*>(out + (long)(r0 + rr) * width) + v;
+        if constexpr (NTS) __builtin_nontemporal_store(pk, dst);
+        else *dst = pk;
       }
     }
   }
@@ -164,26 +167,30 @@ __global__ void k_inverse_perm(int n, const int32_t* __restrict__ p, int32_t* __
 
 template <typename E, int MAXV>
 hipError_t permute_v_launch(int rows, int width, const void* in, const int32_t* rmap,
-                            const int32_t* idx, void* out, hipStream_t s) {
+                            const int32_t* idx, void* out, bool nt_store, hipStream_t s) {
   constexpr int NTHR = 512, RPW = 2;
   const int grid = (rows + RPW - 1) / RPW;
-  hipLaunchKernelGGL((k_permute_rows_v<E, NTHR, RPW, MAXV>), dim3(grid), dim3(NTHR),
-                     RPW * width * sizeof(E), s, rows, width, (const E*)in, rmap, idx, (E*)out);
+  if (nt_store)
+    hipLaunchKernelGGL((k_permute_rows_v<E, NTHR, RPW, MAXV, true>), dim3(grid), dim3(NTHR),
+                       RPW * width * sizeof(E), s, rows, width, (const E*)in, rmap, idx, (E*)out);
+  else
+    hipLaunchKernelGGL((k_permute_rows_v<E, NTHR, RPW, MAXV, false>), dim3(grid), dim3(NTHR),
+                       RPW * width * sizeof(E), s, rows, width, (const E*)in, rmap, idx, (E*)out);
   return hipGetLastError();
 }
 
 template <typename E>
 hipError_t permute_impl(int rows, int width, const void* in, const int32_t* rmap,
-                        const int32_t* idx, void* out, hipStream_t s) {
+                        const int32_t* idx, void* out, bool nt_store, hipStream_t s) {
   const size_t bytes = (size_t)width * sizeof(E);
   const int grid = rows < 65536 ? rows : 65536;
   const bool aligned = bytes % 16 == 0 && (uintptr_t)in % 16 == 0 && (uintptr_t)out % 16 == 0 &&
                        (uintptr_t)idx % 16 == 0;
   if (aligned && 2 * bytes <= PERM_LDS_MAX && rows < (1 << 30)) {
     const int nv = (int)(bytes / 16);
-    if (nv <= 512) return permute_v_launch<E, 1>(rows, width, in, rmap, idx, out, s);
-    if (nv <= 1024) return permute_v_launch<E, 2>(rows, width, in, rmap, idx, out, s);
-    return permute_v_launch<E, 4>(rows, width, in, rmap, idx, out, s);
+    if (nv <= 512) return permute_v_launch<E, 1>(rows, width, in, rmap, idx, out, nt_store, s);
+    if (nv <= 1024) return permute_v_launch<E, 2>(rows, width, in, rmap, idx, out, nt_store, s);
+    return permute_v_launch<E, 4>(rows, width, in, rmap, idx, out, nt_store, s);
   }
   if (bytes <= PERM_LDS_MAX) {
     int vec = (bytes % 16 == 0) && ((uintptr_t)in % 16 == 0) && ((uintptr_t)out % 16 == 0);
@@ -248,16 +255,16 @@ hipError_t launch_dequant_i8(long rows, int cols, const int8_t* q, const float* 
 // element sizes: 1 (int8 weights), 2 (bf16), 4 (fp32)
 hipError_t launch_permute_rows_cols(int rows, int width, int es, const void* in,
                                     const int32_t* rmap, const int32_t* idx, void* out,
-                                    hipStream_t s) {
+                                    hipStream_t s, bool nt_store) {
   if (rows <= 0 || width <= 0) return hipSuccess;
-  if (es == 1) return permute_impl<uint8_t>(rows, width, in, rmap, idx, out, s);
-  if (es == 2) return permute_impl<uint16_t>(rows, width, in, rmap, idx, out, s);
-  return permute_impl<uint32_t>(rows, width, in, rmap, idx, out, s);
+  if (es == 1) return permute_impl<uint8_t>(rows, width, in, rmap, idx, out, nt_store, s);
+  if (es == 2) return permute_impl<uint16_t>(rows, width, in, rmap, idx, out, nt_store, s);
+  return permute_impl<uint32_t>(rows, width, in, rmap, idx, out, nt_store, s);
 }
 
 hipError_t launch_permute_cols(int rows, int width, int es, const void* in, const int32_t* idx,
-                               void* out, hipStream_t s) {
-  return launch_permute_rows_cols(rows, width, es, in, nullptr, idx, out, s);
+                               void* out, hipStream_t s, bool nt_store) {
+  return launch_permute_rows_cols(rows, width, es, in, nullptr, idx, out, s, nt_store);
 }
 
 hipError_t launch_transpose(int m, int n, int es, const void* in, void* out, hipStream_t s) {
