@@ -34,6 +34,7 @@ namespace {
 
 constexpr int PW = 32;        // panel width (columns per workgroup)
 constexpr int PAD = 8;        // LDS row padding (bf16) -> conflict-free b128 reads
+
 constexpr int NT = 512;       // threads per workgroup (8 waves: one CU, latency hiding)
 constexpr int NWAVE = NT / 64;
 
@@ -421,9 +422,10 @@ __device__ __forceinline__ void wide_tile(int id, int nwg, int npan, int& blk, i
   pan = L % npan;
 }
 
-// One panel of 32 * CTW columns of block blk; Xs is [32 * CTW][QP].
+// One panel of 32 * CTW columns of block blk, from column J0; Xs is
+// [32 * CTW][QP].
 template <int MODE, int CTW>
-__device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
+__device__ __forceinline__ void wide_body(int k, int blk, int J0, int nblk,
                                           const bf16* __restrict__ Qg, const float* __restrict__ D,
                                           bf16* __restrict__ out_bf, bf16* __restrict__ out_bfT,
                                           float* __restrict__ out_f, bf16* __restrict__ Xs) {
@@ -434,7 +436,6 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
   // step): a second accumulator-sized register set, so panels of at most 64.
   constexpr bool DRES = MODE == MODE_BWD1;
   static_assert(!DRES || CTW <= 2, "register budget");
-  const int J0 = pan * PWW;
   const int lane = threadIdx.x % 64;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64);  // uniform: scalar offsets
   const int col = lane % 32, h = lane / 32;
@@ -620,9 +621,10 @@ __device__ __forceinline__ void wide_body(int k, int blk, int pan, int nblk,
 #pragma unroll
     for (int t = 0; t < RTW; ++t) asm volatile("" : "+v"(qoff[t]));
     {
-      // P += (+-Q) X: Q fragments from L2 two K-steps ahead, X fragments
-      // from LDS one K-step ahead
-      constexpr int QPF = 2, NKX = NKS + NID;
+      // P += (+-Q) X: Q fragments from L2 two K-steps ahead (three in
+      // phase 1, whose Q fragments feed half as many products per byte), X
+      // fragments from LDS one K-step ahead
+      constexpr int QPF = MODE == MODE_BWD1 ? 3 : 2, NKX = NKS + NID;
       uint4 aq[QPF][RTW], bq[2][CTW];
       const uint32_t wbits = cnp_coef(s + 1, k) == 2.f ? 0x4000u : 0x3F80u;
       auto fetch_b = [&](int ks, int sl) {
@@ -722,11 +724,34 @@ __global__ __launch_bounds__(512, 1) void k_cnp_wide(int k, int nmain, int nblk,
   int blk, pan;
   if (CTM != CTT && id < wm) {
     wide_tile(id, wm, 16 / CTM, blk, pan);
-    wide_body<MODE, CTM>(k, blk, pan, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
+    wide_body<MODE, CTM>(k, blk, pan * 32 * CTM, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
   } else {
     wide_tile(id - wm, (int)gridDim.x - wm, 16 / CTT, blk, pan);
-    wide_body<MODE, CTT>(k, nmain + blk, pan, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
+    wide_body<MODE, CTT>(k, nmain + blk, pan * 32 * CTT, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
   }
+}
+
+// Every block in six panels: four of 96 columns, then two of 64 (the
+// forward and phase 2; phase 1 has no registers for a 96-column panel of
+// D^T).  Between 33 and 42 blocks (the Llama-13B MLP's 37) uniform panels
+// waste the CUs: 128-column ones leave 256 - 4 nblk idle, 64-column ones
+// take two rounds.  Six panels a block fill one round, which lasts a
+// 96-column panel.
+template <int MODE>
+__global__ __launch_bounds__(512, 1) void k_cnp_wide6(int k, int nblk,
+                                                      const bf16* __restrict__ Qg,
+                                                      const float* __restrict__ D,
+                                                      bf16* __restrict__ out_bf,
+                                                      bf16* __restrict__ out_bfT,
+                                                      float* __restrict__ out_f) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  bf16* Xs = reinterpret_cast<bf16*>(smem);
+  int blk, pan;
+  wide_tile(blockIdx.x, (int)gridDim.x, 6, blk, pan);
+  if (pan < 4)
+    wide_body<MODE, 3>(k, blk, pan * 96, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
+  else
+    wide_body<MODE, 2>(k, blk, 384 + (pan - 4) * 64, nblk, Qg, D, out_bf, out_bfT, out_f, Xs);
 }
 
 // dtheta[t(i,j)] (+)= gQ[i][j] - gQ[j][i], one workgroup per (row i, block)
@@ -801,7 +826,7 @@ int cu_count() {
 // ones): the split with the fewest panel times, counting a narrower panel
 // as tcost of a wider one (it streams all of Q per step for fewer columns)
 // and one panel per CU at a time.
-int wide_split(int nblk, int ncu, int pm, int pt, double tcost) {
+int wide_split(int nblk, int ncu, int pm, int pt, double tcost, double* time = nullptr) {
   auto rounds = [&](long wg) { return (double)((wg + ncu - 1) / ncu); };
   int best = nblk;
   double tbest = rounds((long)pm * nblk);
@@ -814,6 +839,7 @@ int wide_split(int nblk, int ncu, int pm, int pt, double tcost) {
       best = M;
     }
   }
+  if (time) *time = tbest;
   return best;
 }
 
@@ -825,13 +851,30 @@ hipError_t launch_wide(int nblk, int k, const bf16* Qg, const float* D, bf16* ou
   // registers): 64 and 32
   constexpr int CTM = MODE == MODE_BWD1 ? 2 : 4, CTT = CTM / 2;
   constexpr double TCOST = MODE == MODE_BWD1 ? 0.6 : 0.55;
+  // a round of six-panel blocks (k_cnp_wide6) in 128-column panel times
+  // (measured at 37 blocks: the forward 64 against 77 us)
+  constexpr double T6 = 0.8;
   constexpr size_t lds = (size_t)32 * CTM * (512 + PAD) * sizeof(bf16);
-  static_assert(lds <= 160 * 1024, "LDS budget");
+  constexpr size_t lds6 = (size_t)96 * (512 + PAD) * sizeof(bf16);
+  static_assert(lds <= 160 * 1024 && lds6 <= 160 * 1024, "LDS budget");
+  const int ncu = cu_count();
+  double tsplit = 0;
+  const int nmain = wide_split(nblk, ncu, 16 / CTM, 16 / CTT, TCOST, &tsplit);
+  if constexpr (MODE != MODE_BWD1) {
+    if (T6 * (double)((6L * nblk + ncu - 1) / ncu) < tsplit - 1e-9) {
+      auto kern6 = k_cnp_wide6<MODE>;
+      static const hipError_t attr6 = hipFuncSetAttribute(
+          (const void*)kern6, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds6);
+      if (attr6 != hipSuccess) return attr6;
+      hipLaunchKernelGGL(kern6, dim3((unsigned)(6L * nblk)), dim3(512), lds6, s, k, nblk, Qg, D,
+                         out_bf, out_bfT, out_f);
+      return hipGetLastError();
+    }
+  }
   auto kern = k_cnp_wide<MODE, CTM, CTT>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  const int nmain = wide_split(nblk, cu_count(), 16 / CTM, 16 / CTT, TCOST);
   const long nwg = (long)(16 / CTM) * nmain + (long)(16 / CTT) * (nblk - nmain);
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(512), lds, s, k, nmain, nblk, Qg, D, out_bf,
                      out_bfT, out_f);

@@ -65,7 +65,8 @@ CNP_CASES = [  # nblk, b, k, dtype, sigma
     (32, 256, 4, "bf16", 0.01),
     (5, 256, 2, "bf16", 0.01),
     (3, 512, 5, "bf16", 0.005),
-    (37, 512, 5, "bf16", 0.005),
+    (37, 512, 5, "bf16", 0.005),   # six panels a block: four of 96 columns, two of 64
+    (40, 512, 1, "bf16", 0.005),   # the same, a single step
     (74, 512, 5, "bf16", 0.005),   # 128-column panels for 64 blocks, 64-column ones for 10
     (65, 512, 3, "bf16", 0.005),   # the same split with a single 64-column block
     (64, 512, 4, "bf16", 0.005),   # exactly one round of wide panels, no tail
