@@ -5,10 +5,32 @@
 #include <string.h>
 
 #include <atomic>
+#include <map>
 #include <mutex>
+#include <tuple>
 
 #include "../../include/poetx.h"
 #include "kernels.h"
+
+namespace poetx {
+
+hipError_t lds_opt_in(const void* kern, int bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  int dev = 0;
+  const hipError_t ge = hipGetDevice(&dev);
+  if (ge != hipSuccess) return ge;
+  static std::mutex mu;
+  static std::map<std::tuple<const void*, int, int>, hipError_t> done;
+  const std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_tuple(kern, dev, bytes);
+  const auto it = done.find(key);
+  if (it != done.end()) return it->second;
+  const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  done.emplace(key, e);
+  return e;
+}
+
+}  // namespace poetx
 
 using namespace poetx;
 

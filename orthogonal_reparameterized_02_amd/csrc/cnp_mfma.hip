@@ -798,11 +798,7 @@ hipError_t launch_panel(int nblk, int k, const float* theta, const bf16* Qg, con
   constexpr size_t lds = (size_t)(PW + B) * (B + PAD) * sizeof(bf16);
   static_assert(lds <= 160 * 1024, "LDS budget");
   auto kern = k_cnp_panel<B, MODE>;
-  // the LDS opt-in is a host call; make it once per kernel, not per launch
-  static const hipError_t attr =
-      lds > 64 * 1024 ? hipFuncSetAttribute((const void*)kern,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
-                      : hipSuccess;
+  const hipError_t attr = lds_opt_in((const void*)kern, (int)lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(B / PW, nblk), dim3(NT), lds, s, k, theta, Qg, D, out_bf,
                      out_bfT, out_f);
@@ -863,8 +859,7 @@ hipError_t launch_wide(int nblk, int k, const bf16* Qg, const float* D, bf16* ou
   if constexpr (MODE != MODE_BWD1) {
     if (T6 * (double)((6L * nblk + ncu - 1) / ncu) < tsplit - 1e-9) {
       auto kern6 = k_cnp_wide6<MODE>;
-      static const hipError_t attr6 = hipFuncSetAttribute(
-          (const void*)kern6, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds6);
+      const hipError_t attr6 = lds_opt_in((const void*)kern6, (int)lds6);
       if (attr6 != hipSuccess) return attr6;
       hipLaunchKernelGGL(kern6, dim3((unsigned)(6L * nblk)), dim3(512), lds6, s, k, nblk, Qg, D,
                          out_bf, out_bfT, out_f);
@@ -872,8 +867,7 @@ hipError_t launch_wide(int nblk, int k, const bf16* Qg, const float* D, bf16* ou
     }
   }
   auto kern = k_cnp_wide<MODE, CTM, CTT>;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  const hipError_t attr = lds_opt_in((const void*)kern, (int)lds);
   if (attr != hipSuccess) return attr;
   const long nwg = (long)(16 / CTM) * nmain + (long)(16 / CTT) * (nblk - nmain);
   hipLaunchKernelGGL(kern, dim3((unsigned)nwg), dim3(512), lds, s, k, nmain, nblk, Qg, D, out_bf,

@@ -199,7 +199,7 @@ __global__ __launch_bounds__(GB_NTH, 1) void k_gather_blocks(
 }
 
 hipError_t gb_set_lds(const void* kern, int bytes) {
-  return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return lds_opt_in(kern, bytes);
 }
 
 }  // namespace
@@ -222,12 +222,12 @@ hipError_t launch_gather_blocks(int T, int W, const bf16* A, const int32_t* perm
   const int lds = GB_RS * (2 * W + 16) + 4 * W;
   const int ngrp = (T + GB_TOK - 1) / GB_TOK;
   if (perm) {
-    static const hipError_t attr = gb_set_lds((const void*)k_gather_blocks<true>, GB_RS * (2 * GB_WMAX + 16) + 4 * GB_WMAX);
+    const hipError_t attr = gb_set_lds((const void*)k_gather_blocks<true>, GB_RS * (2 * GB_WMAX + 16) + 4 * GB_WMAX);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(k_gather_blocks<true>, dim3(ngrp), dim3(GB_NTH), lds, s, T, W, A, perm, Ug,
                        Gf, Out, cscale);
   } else {
-    static const hipError_t attr = gb_set_lds((const void*)k_gather_blocks<false>, GB_RS * (2 * GB_WMAX + 16) + 4 * GB_WMAX);
+    const hipError_t attr = gb_set_lds((const void*)k_gather_blocks<false>, GB_RS * (2 * GB_WMAX + 16) + 4 * GB_WMAX);
     if (attr != hipSuccess) return attr;
     hipLaunchKernelGGL(k_gather_blocks<false>, dim3(ngrp), dim3(GB_NTH), lds, s, T, W, A, perm, Ug,
                        Gf, Out, cscale);

@@ -1164,8 +1164,7 @@ __global__ void k_reduce_splits(long n, int S, long stride, const float* __restr
 
 template <typename K>
 hipError_t set_lds(K kern, int bytes) {
-  if (bytes <= 64 * 1024) return hipSuccess;
-  return hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  return lds_opt_in((const void*)kern, bytes);
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -1177,7 +1176,7 @@ hipError_t nt_launch(int batch, int M, int N, int K, const bf16* A, long lda, lo
   if (cscale && N % BN) return hipErrorInvalidValue;  // the scale is read for whole tiles
   constexpr int lds = CF::LDS;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = set_lds(kern, lds);
+  const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
   hipLaunchKernelGGL(kern, dim3(tilesM * tilesN, batch), dim3(CF::NTH), lds, s, M, N, K, A, lda,
@@ -1192,7 +1191,7 @@ hipError_t tn_launch(int batch, int D, int T, int S, const bf16* A, long lda, lo
                      const bf16* B1 = nullptr, long ldb1 = 0) {
   using CF = Cfg<BT, BT, 2, 2>;
   auto kern = k_gemm_tn<BT>;
-  static const hipError_t attr = set_lds(kern, CF::LDS);
+  const hipError_t attr = set_lds(kern, CF::LDS);
   if (attr != hipSuccess) return attr;
   if (nb0 < 0) {  // one operand pair
     nb0 = batch;
@@ -1227,7 +1226,7 @@ hipError_t nt4_launch_t(int batch, int M, int N, int K, const bf16* A, long lda,
   auto kern = k_nt4<EPI, BMODE, SC>;
   constexpr int lds = 5 * 256 * ROWB;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = set_lds(kern, lds);
+  const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
   const int tM = (M + 255) / 256, tN = (N + 255) / 256;
   hipLaunchKernelGGL(kern, dim3(tM * tN, batch), dim3(256), lds, s, M, N, K, A, lda, sA, B, ldb,
@@ -1335,7 +1334,7 @@ hipError_t blocks_launch(int nblk, int T, int width, const bf16* A, const bf16* 
   auto kern = k_blocks<B, TOK, WM, WN>;
   constexpr int lds = B * B * 2 + 2 * TOK * ROWB;
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = set_lds(kern, lds);
+  const hipError_t attr = set_lds(kern, lds);
   if (attr != hipSuccess) return attr;
   // token splits per block: each workgroup loads its G_j (about two token
   // tiles' time) and then streams its tiles, one workgroup per CU, so the
@@ -1419,7 +1418,7 @@ hipError_t tn4_launch_w(int batch, int nb0, int D, int T, int S, const bf16* A0,
   constexpr int NSTG = 4;
   constexpr int lds = NSTG * 32 * (256 + TN) * 2;  // stages of 32 tokens x (A, B) rows
   static_assert(lds <= 160 * 1024, "LDS budget");
-  static const hipError_t attr = set_lds(k_tn4<256, TN, NSTG>, lds);
+  const hipError_t attr = set_lds(k_tn4<256, TN, NSTG>, lds);
   if (attr != hipSuccess) return attr;
   const long dd = (long)D * D;
   const int tilesN = D / TN, ntiles = (D / 256) * tilesN;

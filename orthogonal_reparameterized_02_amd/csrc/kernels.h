@@ -19,6 +19,12 @@ __host__ __device__ inline float cnp_wcoef(int p, int k) {
   return ((p - 1) & 1) ? -cnp_coef(p, k) : cnp_coef(p, k);
 }
 
+// Lets `kern` use `bytes` of dynamic LDS on the calling thread's current
+// device (needed above 64 KB).  The attribute belongs to the (kernel,
+// device) pair, so it is set once per pair and size; later calls return the
+// first call's status (api.hip).
+hipError_t lds_opt_in(const void* kern, int bytes);
+
 // ---- permutations (perm.hip); es = element bytes 1 | 2 | 4 ----------------
 hipError_t launch_fold(int m, int n, int es, const void* W0, const int32_t* pR,
                        const int32_t* pP, void* W0f, void* W0fT, int32_t* pRinv,
